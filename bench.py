@@ -1,0 +1,224 @@
+"""Benchmark of one GPU's share of the expert-parallel MoE layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode128_fp8]
+
+A step is one whole layer (dispatch -> grouped GEMM with SwiGLU + requant -> combine)
+over one batch of synthetic input already resident in HBM.  The default workload is
+the 128-token decode layer: 8 simulated source ranks x 16 tokens, hidden 7168, 32
+local experts, top-8, intermediate 2048, FP8 e4m3 weights (128x128 scales) and
+activations (1x128 scales), bf16 output.
+
+Prints ONE JSON line: value = layer latency in microseconds (lower is better), with
+per-stage timings from HIP events recorded by the library on the launch stream,
+dispatch/combine GB/s, grouped-GEMM TFLOP/s, the roofline of the dominant kernel
+(GEMM1) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer µs at 1–256 tok/GPU; dispatch/combine GB/s; grouped-GEMM TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+GEMM1_SRC = os.path.join(ROOT, "combine_top_gate_amd", "csrc", "gemm_lowp.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_decode128_fp8_traffic.md")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode128_fp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=32,
+                    help="experts the CPU oracle evaluates in each timed sample")
+    ap.add_argument("--cpu-repeats", type=int, default=3,
+                    help="timed CPU oracle samples (the median is reported)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(inp, cnt):
+    """HBM bytes each stage must move at least once (the per-unit figures are in the design notes)."""
+    S, T_s, H, I, E, k = inp.S, inp.T_s, inp.H, inp.I, inp.E, inp.k
+    T, R = S * T_s, int(cnt.sum())
+    active = int((cnt.sum(axis=0) > 0).sum())
+    Ish = inp.shared_I
+    if inp.weight == "fp8":
+        w13 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+        w2 = H * I + (H // 128) * (I // 128) * 4
+        w13_sh = w2_sh = 0
+    else:  # MXFP4: packed nibbles + one e8m0 byte per 32
+        w13 = 2 * I * H // 2 + 2 * I * H // 32
+        w2 = H * I // 2 + H * I // 32
+        w13_sh = 2 * Ish * H // 2 + 2 * Ish * H // 32
+        w2_sh = H * Ish // 2 + H * Ish // 32
+    xrow = H + (H // 128) * 4
+    hrow = I + (I // 128) * 4
+    hrow_sh = Ish + (Ish // 128) * 4 if Ish else 0
+    d = {}
+    # dispatch: ids read, each source row read once, R window rows (+scales) written, control state
+    d["dispatch"] = T * k * 4 + T * xrow + R * xrow + T * k * 4 + S * T_s * k * 4 + 2 * S * E * 4
+    # GEMM1: weights of active experts once, window rows read, h rows written
+    d["gemm1"] = active * w13 + R * xrow + R * hrow + (w13_sh + T * xrow + T * hrow_sh if Ish else 0)
+    # GEMM2: weights once, h rows read, y rows (bf16) written
+    d["gemm2"] = active * w2 + R * hrow + R * H * 2 + (w2_sh + T * hrow_sh + T * H * 2 if Ish else 0)
+    # combine: y rows read, weights and rows read, token rows written
+    d["combine"] = R * H * 2 + T * k * 8 + T * H * 2 + (T * H * 2 if Ish else 0)
+    d["layer"] = sum(d.values())
+    flops = 2 * R * (2 * I) * H + 2 * R * I * H + (6 * T * Ish * H if Ish else 0)
+    return d, flops
+
+
+def read_traffic():
+    """GEMM1 HBM bytes per launch from the committed counter summary, if it is for this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(GEMM1_SRC, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline(inp, n_experts, repeats):
+    """The oracle as it stands, timed on a bounded sample of the same workload.
+
+    Sample: the full dispatch and combine, and the expert FFN (dequantise, GEMM1,
+    SwiGLU, requant, GEMM2) of n_experts of the E experts, the expert part scaled
+    by E / n_experts to the whole layer; median of `repeats` samples."""
+    runs = [_cpu_once(inp, n_experts) for _ in range(max(1, repeats))]
+    runs.sort(key=lambda r: r[0])
+    total, wall, n, cores = runs[len(runs) // 2]
+    what = "the whole layer" if n == inp.E else f"dispatch + combine + the FFNs of {n} of {inp.E} experts (scaled by {inp.E}/{n})"
+    return {"value": round(total * 1e6, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
+            "sample": f"{what}, one batch of the same workload; median of {len(runs)} runs of "
+                      f"{wall:.1f} s wall each"}
+
+
+def _cpu_once(inp, n_experts):
+    from oracle import layer
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    route = layer.dispatch(inp.ids, inp.E)
+    rows = layer.expert_rows(route["cnt"], route["off"], inp.T_s, inp.k)
+    t1 = time.perf_counter()
+    x = np.asarray(inp.x).reshape(inp.S * inp.T_s, inp.H)
+    xs = np.asarray(inp.x_scale).reshape(inp.S * inp.T_s, inp.H // 128)
+    xt = layer.dequant_act_fp8(x, xs)
+    R = inp.S * inp.T_s * inp.k
+    y = np.zeros((R, inp.H))
+    src = np.where(route["row_src"] >= 0, route["row_src"] // inp.k, -1)
+    n = min(n_experts, inp.E)
+    for e in range(n):
+        r = rows[e]
+        w13 = layer.dequant_weight(inp.weight, inp.w13[e], inp.s13[e])
+        w2 = layer.dequant_weight(inp.weight, inp.w2[e], inp.s2[e])
+        ye, _, _ = layer.expert_ffn(xt[src[r]], w13, w2, inp.I, True)
+        y[r] = layer.round_out(ye, inp.out)
+    t2 = time.perf_counter()
+    layer.combine(y, route["dst_row"], inp.topk_w)
+    t3 = time.perf_counter()
+    total = (t1 - t0) + (t2 - t1) * inp.E / n + (t3 - t2)
+    return total, t3 - t0, n, cores
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not "
+              "part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from combine_top_gate_amd import binding, synth
+
+    torch.cuda.set_device(0)
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(args.workload)
+    d = binding.DeviceInputs(inp)
+    moe = binding.Moe.for_inputs(inp)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        moe.run(d)
+    torch.cuda.synchronize()
+    cnt = moe.routing(inp.S, inp.T_s, inp.k, inp.E)[0].cpu().numpy()
+    moe.set_timing(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.run(d)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms, ncalls = moe.read_timing()
+    assert ncalls == args.steps
+    if moe.device_error():
+        raise RuntimeError("device error during the timed region")
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg = [m / ncalls for m in stage_ms]  # dispatch, gemm1, gemm2, combine, layer (ms)
+    nbytes, flops = algorithmic_bytes(inp, cnt)
+    gbps = lambda b, ms: b / (ms * 1e-3) / 1e9
+    g1_gbps = gbps(nbytes["gemm1"], avg[1])
+    traffic = read_traffic()
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_step * 1e3, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if inp.act == "fp8" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "sources": inp.S, "tokens_per_source": inp.T_s,
+                   "tokens": inp.S * inp.T_s, "hidden": inp.H, "inter": inp.I, "experts": inp.E,
+                   "topk": inp.k, "weights": inp.weight, "shared_inter": inp.shared_I,
+                   "routing": inp.extra.get("routing"), "schedule": "fence"},
+        "stages_us": {"dispatch": round(avg[0] * 1e3, 2), "gemm1": round(avg[1] * 1e3, 2),
+                      "gemm2": round(avg[2] * 1e3, 2), "combine": round(avg[3] * 1e3, 2),
+                      "layer_events": round(avg[4] * 1e3, 2)},
+        "dispatch_GBps": round(gbps(nbytes["dispatch"], avg[0]), 1),
+        "combine_GBps": round(gbps(nbytes["combine"], avg[3]), 1),
+        "gemm_TFLOPs": round(flops / ((avg[1] + avg[2]) * 1e-3) / 1e12, 2),
+        "layer_hbm_frac": round(gbps(nbytes["layer"], ms_step) / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"kernel": "gemm1 (FP8 grouped GEMM + SwiGLU + requant)", "bound": "hbm",
+                     "achieved": round(g1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(g1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes["gemm1"]},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_experts, args.cpu_repeats)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,406 @@
+// Host side of the C-ABI: argument validation, workspace, launch sequencing, timing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int kStages = 5;  // dispatch, gemm1, gemm2, combine, layer
+
+}  // namespace
+
+struct moe_ctx {
+  moe_config cfg{};
+  int device = 0;
+  int64_t R_cap = 0, rows_cap = 0;
+  int hstride = 0;  // elements per h row = max(I, Ish)
+  int row_bytes = 0;
+  // workspace
+  uint8_t* win = nullptr;
+  float* wsc = nullptr;
+  uint8_t* h = nullptr;
+  float* hs = nullptr;
+  void* y = nullptr;
+  int32_t* cnt = nullptr;
+  int32_t* off = nullptr;
+  int32_t* dst_row = nullptr;
+  int32_t* row_src = nullptr;
+  uint32_t* err = nullptr;
+  // state of the last dispatch
+  int T_s = -1;
+  SrcPtrs src{};
+  // timing
+  int timing_cap = 0, timing_n = 0;
+  std::vector<hipEvent_t> ev;  // timing_cap x (kStages+1)
+};
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+BatchDims dims(const moe_ctx* c) {
+  BatchDims d;
+  d.S = c->cfg.n_src;
+  d.T_s = c->T_s;
+  d.k = c->cfg.topk;
+  d.E = c->cfg.n_experts;
+  d.H = c->cfg.hidden;
+  d.I = c->cfg.inter;
+  d.Ish = c->cfg.shared_inter;
+  d.R = d.S * d.T_s * d.k;
+  d.T = d.S * d.T_s;
+  d.hstride = c->hstride;
+  return d;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->n_src < 1 || c->n_src > MOE_MAX_SRC)
+    return fail(MOE_ERR_INVALID_ARG, "n_src %d outside 1..%d", c->n_src, MOE_MAX_SRC);
+  if (c->max_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "max_tokens %d < 0", c->max_tokens);
+  if (c->hidden <= 0 || c->hidden % 128)
+    return fail(MOE_ERR_INVALID_ARG, "hidden %d is not a positive multiple of 128", c->hidden);
+  if (c->inter <= 0 || c->inter % 128)
+    return fail(MOE_ERR_INVALID_ARG, "inter %d is not a positive multiple of 128", c->inter);
+  if (c->shared_inter < 0 || c->shared_inter % 128)
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter %d is not a multiple of 128", c->shared_inter);
+  if (c->n_experts < 1 || c->n_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts %d outside 1..%d", c->n_experts, MOE_MAX_EXPERTS);
+  if (c->topk < 1 || c->topk > MOE_MAX_TOPK || c->topk > c->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "topk %d outside 1..min(%d, n_experts)", c->topk, MOE_MAX_TOPK);
+  const bool fp8 = c->act == MOE_FP8_E4M3 && (c->weight == MOE_FP8_E4M3 || c->weight == MOE_FP4_E2M1) &&
+                   c->out == MOE_BF16;
+  const bool f32 = c->act == MOE_F32 && c->weight == MOE_F32 && c->out == MOE_F32;
+  if (!fp8 && !f32)
+    return fail(MOE_ERR_INVALID_ARG,
+                "dtype combination act=%d weight=%d out=%d is not one of (fp8, fp8|fp4, bf16) or "
+                "(f32, f32, f32)",
+                c->act, c->weight, c->out);
+  if (c->sched != MOE_SCHED_FENCE && c->sched != MOE_SCHED_SENTINEL)
+    return fail(MOE_ERR_INVALID_ARG, "unknown schedule %d", c->sched);
+  const int64_t R = (int64_t)c->n_src * c->max_tokens * c->topk;
+  if (R > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "window of %lld rows is too large", (long long)R);
+  return MOE_OK;
+}
+
+// 16-token tiles per pass of the low-precision GEMMs: enough for a typical expert
+// (mean rows + two standard deviations of a multinomial count) in one pass.
+int tok_tiles(const BatchDims& d) {
+  const double mean = (double)d.R / d.E;
+  const double want = mean + 2.0 * std::sqrt(mean);
+  int nt = (int)std::ceil(want / 16.0);
+  return std::min(6, std::max(1, nt));
+}
+
+void record(moe_ctx* c, int stage, hipStream_t st) {
+  if (c->timing_n < c->timing_cap) (void)hipEventRecord(c->ev[(size_t)c->timing_n * (kStages + 1) + stage], st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error_message(void) { return g_msg; }
+
+moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->sched == MOE_SCHED_SENTINEL)
+    return fail(MOE_ERR_UNSUPPORTED, "the SENTINEL schedule is not available in this build");
+  moe_ctx* c = new moe_ctx();
+  c->cfg = *cfg;
+  auto cleanup = [&](moe_status s) {
+    moe_destroy(c);
+    return s;
+  };
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) return cleanup(fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e)));
+  const bool f32 = cfg->act == MOE_F32;
+  const int S = cfg->n_src, Tc = cfg->max_tokens, k = cfg->topk, E = cfg->n_experts, H = cfg->hidden;
+  c->R_cap = (int64_t)S * Tc * k;
+  c->rows_cap = c->R_cap + (int64_t)S * Tc;
+  c->hstride = std::max(cfg->inter, cfg->shared_inter);
+  c->row_bytes = f32 ? 4 * H : H;
+  const size_t one = 1;
+  auto alloc = [&](void** p, size_t bytes) {
+    return hipMalloc(p, std::max(bytes, one));
+  };
+  if ((e = alloc((void**)&c->win, (size_t)c->R_cap * c->row_bytes)) != hipSuccess ||
+      (e = alloc((void**)&c->wsc, f32 ? 0 : (size_t)c->R_cap * (H / 128) * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->h, (size_t)c->rows_cap * c->hstride * (f32 ? 4 : 1))) != hipSuccess ||
+      (e = alloc((void**)&c->hs, f32 ? 0 : (size_t)c->rows_cap * (c->hstride / 128) * 4)) != hipSuccess ||
+      (e = alloc(&c->y, (size_t)c->rows_cap * H * (f32 ? 4 : 2))) != hipSuccess ||
+      (e = alloc((void**)&c->cnt, (size_t)S * E * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->off, (size_t)S * E * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->dst_row, (size_t)S * Tc * k * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->row_src, (size_t)c->R_cap * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->err, 4)) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "workspace allocation failed: %s", hipGetErrorString(e)));
+  if ((e = hipMemset(c->err, 0, 4)) != hipSuccess || (e = hipMemset(c->cnt, 0, (size_t)S * E * 4)) != hipSuccess ||
+      (e = hipMemset(c->off, 0, (size_t)S * E * 4)) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)));
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_destroy(moe_ctx* c) {
+  if (!c) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  for (auto ev : c->ev) (void)hipEventDestroy(ev);
+  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y, c->cnt, c->off, c->dst_row, c->row_src, c->err};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  delete c;
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                        const int32_t* ids, hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  const moe_config& cf = c->cfg;
+  if (T_s < 0 || T_s > cf.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "tokens_per_src %d outside 0..max_tokens (%d)", T_s, cf.max_tokens);
+  const bool fp8 = cf.act == MOE_FP8_E4M3;
+  if (T_s > 0) {
+    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (fp8 && !x_scale) return fail(MOE_ERR_INVALID_ARG, "x_scale is NULL for FP8 activations");
+    if (!ids) return fail(MOE_ERR_INVALID_ARG, "ids is NULL");
+    for (int s = 0; s < cf.n_src; ++s) {
+      if (!x[s] || !aligned16(x[s])) return fail(MOE_ERR_INVALID_ARG, "x[%d] is NULL or not 16-byte aligned", s);
+      if (fp8 && (!x_scale[s] || ((uintptr_t)x_scale[s] & 3u)))
+        return fail(MOE_ERR_INVALID_ARG, "x_scale[%d] is NULL or misaligned", s);
+    }
+  }
+  SrcPtrs src{};
+  for (int s = 0; s < cf.n_src && T_s > 0; ++s) {
+    src.x[s] = static_cast<const uint8_t*>(x[s]);
+    src.xs[s] = fp8 ? x_scale[s] : nullptr;
+  }
+  c->T_s = T_s;
+  c->src = src;
+  if (T_s == 0) return MOE_OK;
+  RouteArgs ra{ids, c->cnt, c->off, c->dst_row, c->row_src, c->err, cf.n_src, T_s, cf.topk, cf.n_experts};
+  HIP_TRY(launch_route(ra, stream));
+  ScatterArgs sa{src, c->dst_row, c->win, fp8 ? c->wsc : nullptr, cf.n_src, T_s, cf.topk, c->row_bytes,
+                 fp8 ? cf.hidden / 128 : 0};
+  HIP_TRY(launch_scatter(sa, stream));
+  return MOE_OK;
+}
+
+static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed) {
+  const moe_config& cf = c->cfg;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
+  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1;
+  if (!w->w13 || !w->w2 || (!f32 && (!w->s13 || !w->s2)))
+    return fail(MOE_ERR_INVALID_ARG, "routed expert weight or scale pointer is NULL");
+  if (!aligned16(w->w13) || !aligned16(w->w2)) return fail(MOE_ERR_INVALID_ARG, "weights not 16-byte aligned");
+  if (cf.shared_inter) {
+    if (!w->sh_w13 || !w->sh_w2 || (!f32 && (!w->sh_s13 || !w->sh_s2)))
+      return fail(MOE_ERR_INVALID_ARG, "shared expert weight or scale pointer is NULL");
+    if (!aligned16(w->sh_w13) || !aligned16(w->sh_w2))
+      return fail(MOE_ERR_INVALID_ARG, "shared weights not 16-byte aligned");
+  }
+  if (c->T_s == 0) {
+    if (timed) { record(c, 2, stream); }
+    return MOE_OK;
+  }
+  const BatchDims d = dims(c);
+  const int64_t H = cf.hidden, I = cf.inter;
+  GemmArgs g{};
+  g.d = d;
+  g.cnt = c->cnt;
+  g.off = c->off;
+  g.src = c->src;
+  g.err = c->err;
+  // GEMM1
+  g.w = static_cast<const uint8_t*>(w->w13);
+  g.ws = w->s13;
+  g.w_sh = static_cast<const uint8_t*>(w->sh_w13);
+  g.ws_sh = w->sh_s13;
+  if (f32) {
+    g.w_stride = 2 * I * H * 4;
+  } else if (fp4) {
+    g.w_stride = 2 * I * (H / 2);
+    g.ws_stride = 2 * I * (H / 32);
+  } else {
+    g.w_stride = 2 * I * H;
+    g.ws_stride = (2 * I / 128) * (H / 128);
+  }
+  g.a = c->win;
+  g.as = c->wsc;
+  g.h = c->h;
+  g.hs = c->hs;
+  const int nt = tok_tiles(d);
+  HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, nt, stream));
+  if (timed) record(c, 2, stream);
+  // GEMM2
+  g.w = static_cast<const uint8_t*>(w->w2);
+  g.ws = w->s2;
+  g.w_sh = static_cast<const uint8_t*>(w->sh_w2);
+  g.ws_sh = w->sh_s2;
+  if (f32) {
+    g.w_stride = H * I * 4;
+  } else if (fp4) {
+    g.w_stride = H * (I / 2);
+    g.ws_stride = H * (I / 32);
+  } else {
+    g.w_stride = H * I;
+    g.ws_stride = (H / 128) * (I / 128);
+  }
+  g.a = c->h;
+  g.as = c->hs;
+  g.y = static_cast<uint16_t*>(c->y);
+  g.yf = static_cast<float*>(c->y);
+  HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, nt, stream));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(moe_ctx* c, const moe_weights* w, hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  return gemm_stage(c, w, stream, false);
+}
+
+moe_status moe_combine(moe_ctx* c, const float* topk_w, void* out, hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine before any moe_dispatch");
+  if (c->T_s == 0) return MOE_OK;
+  if (!topk_w || !out) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
+  if (!aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "out is not 16-byte aligned");
+  const moe_config& cf = c->cfg;
+  const BatchDims d = dims(c);
+  CombineArgs a{c->dst_row, topk_w, c->y, out, d.T, d.k, d.H, d.R, cf.shared_inter > 0, cf.out == MOE_F32};
+  HIP_TRY(launch_combine(a, stream));
+  return MOE_OK;
+}
+
+moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                     const int32_t* ids, const float* topk_w, const moe_weights* w, void* out,
+                     hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (T_s > 0 && (!topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
+  const bool timed = c->timing_n < c->timing_cap;
+  if (timed) record(c, 0, stream);
+  moe_status st = moe_dispatch(c, T_s, x, x_scale, ids, stream);
+  if (st != MOE_OK) return st;
+  if (timed) record(c, 1, stream);
+  st = gemm_stage(c, w, stream, timed);
+  if (st != MOE_OK) return st;
+  if (timed) record(c, 3, stream);
+  st = moe_combine(c, topk_w, out, stream);
+  if (st != MOE_OK) return st;
+  if (timed) {
+    record(c, 4, stream);
+    c->timing_n++;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_get_routing(moe_ctx* c, int32_t* cnt, int32_t* off, int32_t* dst_row, int32_t* row_src,
+                           hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "no dispatch yet");
+  const moe_config& cf = c->cfg;
+  const size_t SE = (size_t)cf.n_src * cf.n_experts * 4, R = (size_t)cf.n_src * c->T_s * cf.topk * 4;
+  if (cnt) HIP_TRY(hipMemcpyAsync(cnt, c->cnt, SE, hipMemcpyDeviceToDevice, stream));
+  if (off) HIP_TRY(hipMemcpyAsync(off, c->off, SE, hipMemcpyDeviceToDevice, stream));
+  if (dst_row && R) HIP_TRY(hipMemcpyAsync(dst_row, c->dst_row, R, hipMemcpyDeviceToDevice, stream));
+  if (row_src && R) HIP_TRY(hipMemcpyAsync(row_src, c->row_src, R, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+moe_status moe_copy_buffer(moe_ctx* c, moe_buffer which, void* dst, size_t bytes, hipStream_t stream) {
+  if (!c || !dst) return fail(MOE_ERR_INVALID_ARG, "ctx or dst is NULL");
+  const bool f32 = c->cfg.act == MOE_F32;
+  const int H = c->cfg.hidden;
+  const void* src = nullptr;
+  size_t cap = 0;
+  switch (which) {
+    case MOE_BUF_WINDOW: src = c->win; cap = (size_t)c->R_cap * c->row_bytes; break;
+    case MOE_BUF_WSCALE: src = c->wsc; cap = f32 ? 0 : (size_t)c->R_cap * (H / 128) * 4; break;
+    case MOE_BUF_H: src = c->h; cap = (size_t)c->rows_cap * c->hstride * (f32 ? 4 : 1); break;
+    case MOE_BUF_HSCALE: src = c->hs; cap = f32 ? 0 : (size_t)c->rows_cap * (c->hstride / 128) * 4; break;
+    case MOE_BUF_Y: src = c->y; cap = (size_t)c->rows_cap * H * (f32 ? 4 : 2); break;
+    default: return fail(MOE_ERR_INVALID_ARG, "unknown buffer %d", (int)which);
+  }
+  if (bytes > cap) return fail(MOE_ERR_INVALID_ARG, "%zu bytes requested, buffer holds %zu", bytes, cap);
+  if (bytes) HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {
+  if (!c || !bits) return fail(MOE_ERR_INVALID_ARG, "ctx or bits is NULL");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(bits, c->err, 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemset(c->err, 0, 4));
+  return MOE_OK;
+}
+
+moe_status moe_set_timing(moe_ctx* c, int32_t max_calls) {
+  if (!c || max_calls < 0) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL or max_calls < 0");
+  HIP_TRY(hipDeviceSynchronize());
+  for (auto ev : c->ev) (void)hipEventDestroy(ev);
+  c->ev.assign((size_t)max_calls * (kStages + 1), nullptr);
+  for (auto& ev : c->ev) HIP_TRY(hipEventCreate(&ev));
+  c->timing_cap = max_calls;
+  c->timing_n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_read_timing(moe_ctx* c, float* ms, int32_t* n_calls) {
+  if (!c || !ms || !n_calls) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  for (int i = 0; i < kStages; ++i) ms[i] = 0.f;
+  for (int n = 0; n < c->timing_n; ++n) {
+    hipEvent_t* e = &c->ev[(size_t)n * (kStages + 1)];
+    HIP_TRY(hipEventSynchronize(e[4]));
+    float t;
+    // events: 0 start, 1 after dispatch, 2 after GEMM1, 3 after GEMM2, 4 after combine
+    for (int i = 0; i < 4; ++i) {
+      HIP_TRY(hipEventElapsedTime(&t, e[i], e[i + 1]));
+      ms[i] += t;
+    }
+    HIP_TRY(hipEventElapsedTime(&t, e[0], e[4]));
+    ms[4] += t;
+  }
+  *n_calls = c->timing_n;
+  c->timing_n = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Launchers of the HIP kernels; the host API (api.hip) is their only caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+// ---- dispatch ---------------------------------------------------------------
+struct RouteArgs {
+  const int32_t* ids;  // [S][T_s][k]
+  int32_t* cnt;        // [S][E]
+  int32_t* off;        // [S][E]
+  int32_t* dst_row;    // [S][T_s][k]
+  int32_t* row_src;    // [S*T_s*k]
+  uint32_t* err;
+  int S, T_s, k, E;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct ScatterArgs {
+  SrcPtrs src;
+  const int32_t* dst_row;  // [S][T_s][k]
+  uint8_t* win;            // [R][row_bytes]
+  float* wsc;              // [R][nsc] or null
+  int S, T_s, k;
+  int row_bytes;           // bytes per token row (multiple of 16)
+  int nsc;                 // scales per row (0 = none)
+};
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
+
+// ---- grouped GEMMs ----------------------------------------------------------
+// One launch covers every routed expert and, when present, the shared expert
+// (group index E), which reads token rows straight from the source buffers.
+struct GemmArgs {
+  BatchDims d;
+  const int32_t* cnt;
+  const int32_t* off;
+  // weights: routed base + per-expert strides, and the shared expert
+  const uint8_t* w;
+  const void* ws;
+  int64_t w_stride;   // bytes per routed expert
+  int64_t ws_stride;  // scale elements per routed expert
+  const uint8_t* w_sh;
+  const void* ws_sh;
+  // activation rows (GEMM1: the window; GEMM2: the h window) and their scales
+  const uint8_t* a;
+  const float* as;
+  SrcPtrs src;        // GEMM1 shared expert rows
+  // outputs
+  uint8_t* h;         // GEMM1: [R+T][hstride]
+  float* hs;          // GEMM1: [R+T][hstride/128]
+  uint16_t* y;        // GEMM2 (bf16): [R+T][H]
+  float* yf;          // GEMM2 (F32): [R+T][H]
+  uint32_t* err;
+};
+// weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; tok_tiles: 16-token tiles per pass (1..6)
+hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st);
+hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st);
+hipError_t launch_gemm1_f32(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_f32(const GemmArgs& a, hipStream_t st);
+
+// ---- combine ----------------------------------------------------------------
+struct CombineArgs {
+  const int32_t* dst_row;  // [S][T_s][k]
+  const float* topk_w;     // [S][T_s][k]
+  const void* y;           // [R+T][H] bf16 or f32
+  void* out;               // [S][T_s][H]
+  int T, k, H, R;
+  int has_shared;
+  int out_f32;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);

@@ -1,0 +1,211 @@
+/*
+ * ctg_moe.h -- C-ABI of one MI355X's share of an expert-parallel MoE layer.
+ *
+ * The layer has three steps, each an entry point below, plus one call that runs
+ * all three:
+ *
+ *   moe_dispatch      tokens arriving from S source ranks are pushed, with no
+ *                     metadata exchanged first, into rank-major receive buffers
+ *                     ("windows") in this GPU's HBM.  Source s owns window rows
+ *                     [s*T_s*k, (s+1)*T_s*k) and lays its (token, slot) pairs out
+ *                     sorted by expert using only its own counts.
+ *                     ["One-Sided Expert-Parallel All-to-All for Mixture-of-Experts
+ *                     Inference over NVLink", abstract: one-sided push into
+ *                     rank-major buffers without a metadata exchange; "Relay Buffer
+ *                     Independent Communication over Pooled HBM for Efficient MoE
+ *                     Inference on Ascend", abstract: direct placement into
+ *                     destination expert windows, counts/offsets/sync state only.]
+ *   moe_grouped_gemm  per local expert, the windows are read in place by an FP8
+ *                     (or MXFP4) block-scaled grouped GEMM with the SwiGLU
+ *                     activation and the FP8 requantisation of its output fused,
+ *                     followed by the down projection; an optional shared expert
+ *                     runs over every token, reading the source buffers in place.
+ *                     ["One-Sided ... over NVLink", abstract: grouped GEMMs read
+ *                     the buffers in place; "GC-MoE: Overlapping Expert-Parallel
+ *                     Token Dispatch with FP8/FP4 Grouped GEMM via CUDA Green
+ *                     Contexts", full text: block-scaled MMA with fused SwiGLU,
+ *                     requantization and optional shared experts.]
+ *   moe_combine       every token's k expert outputs are read back from the
+ *                     windows, weighted by its top-k gate weights and summed in
+ *                     token order (plus the shared expert's output).
+ *                     ["Relay Buffer Independent Communication ...", abstract:
+ *                     direct reading from expert windows, less output restoration.]
+ *
+ * Synchronisation between dispatch and GEMM follows one of two schedules
+ * ["One-Sided ... over NVLink", abstract: Fence for throughput, Sentinel for
+ * latency].  FENCE: the steps run in stream order.  SENTINEL: dispatch runs on
+ * a stream restricted to a few CUs while the GEMM kernel is already resident on
+ * the others; each source publishes an epoch tag once its rows and counts are in
+ * place and the GEMM polls those tags before it reads a window (the device-side
+ * counter handshake of "GC-MoE", full text, and of "GC-MoE: Decoupling MoE
+ * Communication and Computation with CUDA Green Contexts", section "Three-Node
+ * CUDA Graph and token-ring Handshake").  Epoch tags grow monotonically, so no
+ * clean pass is needed between calls.
+ *
+ * Conventions
+ *   - Every data pointer is a DEVICE pointer owned by the caller, except the
+ *     arrays of per-source pointers (x, x_scale), which are HOST arrays of S
+ *     device pointers.  The context owns its workspace (windows, control state).
+ *   - Row-major layouts; FP8 is OCP e4m3 ("e4m3fn": bias 7, max 448, no inf);
+ *     FP4 is OCP e2m1 with element 2i in the low nibble of byte i; e8m0 scale
+ *     bytes mean 2^(b-127).
+ *   - Block scales are fp32 multipliers (real value = code value * scale):
+ *     activations 1x128 along the hidden dimension; FP8 weights 128x128 over
+ *     (output row, input column); MXFP4 weights e8m0 per 1x32 along the input.
+ *   - All calls are asynchronous on the given stream (0 = the null stream) and
+ *     allocate nothing except moe_create.  A context is not thread-safe; calls on
+ *     one context must be issued on one stream (or be ordered by the caller).
+ *   - Arguments are validated on the host before any work is enqueued; a
+ *     non-OK status means nothing was enqueued, and moe_last_error_message()
+ *     gives the reason.  Conditions found on the device (an expert id outside
+ *     [-1, E), a sentinel wait that timed out) are latched in a device error
+ *     word read by moe_last_device_error().
+ */
+#ifndef CTG_MOE_H
+#define CTG_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_SRC 32      /* simulated source ranks */
+#define MOE_MAX_EXPERTS 256 /* local routed experts */
+#define MOE_MAX_TOPK 16
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or dtype combination */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_HIP = 3,         /* a HIP runtime call failed (no device, out of memory, ...) */
+  MOE_ERR_DEVICE = 4       /* a device-side condition was latched; see moe_last_device_error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype;
+
+typedef enum { MOE_SCHED_FENCE = 0, MOE_SCHED_SENTINEL = 1 } moe_schedule;
+
+/* device error bits (moe_last_device_error) */
+#define MOE_DEVERR_BAD_ID 0x1u  /* an expert id outside [-1, E); that pair was dropped */
+#define MOE_DEVERR_TIMEOUT 0x2u /* a sentinel wait gave up; the GEMM output is invalid */
+
+typedef struct moe_config {
+  int32_t n_src;          /* S: simulated source ranks, 1..MOE_MAX_SRC */
+  int32_t max_tokens;     /* capacity T_cap: largest tokens-per-source of any call */
+  int32_t hidden;         /* H, multiple of 128 */
+  int32_t inter;          /* I of the routed experts, multiple of 128 */
+  int32_t n_experts;      /* E local routed experts, 1..MOE_MAX_EXPERTS */
+  int32_t topk;           /* k, 1..MOE_MAX_TOPK */
+  int32_t shared_inter;   /* I of the one shared expert, multiple of 128; 0 = none */
+  moe_dtype act;          /* MOE_FP8_E4M3 (with 1x128 scales) or MOE_F32 */
+  moe_dtype weight;       /* MOE_FP8_E4M3 or MOE_FP4_E2M1 (with MOE_FP8_E4M3 act), or MOE_F32 */
+  moe_dtype out;          /* MOE_BF16 (FP8 act) or MOE_F32 (F32 act) */
+  moe_schedule sched;     /* FENCE or SENTINEL */
+  int32_t dispatch_cus;   /* SENTINEL: CUs given to dispatch (0 = default) */
+} moe_config;
+
+/*
+ * Expert weights, all device pointers, row-major:
+ *   FP8:   w13 u8  [E][2I][H]   s13 f32 [E][2I/128][H/128]
+ *          w2  u8  [E][H][I]    s2  f32 [E][H/128][I/128]
+ *   MXFP4: w13 u8  [E][2I][H/2] s13 u8 (e8m0) [E][2I][H/32]
+ *          w2  u8  [E][H][I/2]  s2  u8 (e8m0) [E][H][I/32]
+ *   F32:   w13 f32 [E][2I][H], w2 f32 [E][H][I], s13 = s2 = NULL
+ * Rows 0..I-1 of W13[e] are the gate projection, rows I..2I-1 the up projection.
+ * The shared expert (sh_*) has the same layout with E = 1 and I = shared_inter;
+ * its pointers are ignored when shared_inter = 0.
+ */
+typedef struct moe_weights {
+  const void *w13, *s13, *w2, *s2;
+  const void *sh_w13, *sh_s13, *sh_w2, *sh_s2;
+} moe_weights;
+
+typedef struct moe_ctx moe_ctx;
+
+/* Internal buffers that moe_copy_buffer can read (parity tests of intermediate steps). */
+typedef enum {
+  MOE_BUF_WINDOW = 0,   /* dispatched rows: [R][H] bytes (FP8) or [R][H] f32, R = S*T_s*k */
+  MOE_BUF_WSCALE = 1,   /* their scales: f32 [R][H/128] (FP8 act only) */
+  MOE_BUF_H = 2,        /* SwiGLU output: FP8 [R + T][I] (or f32 for F32 act); rows R.. = shared expert */
+  MOE_BUF_HSCALE = 3,   /* its 1x128 scales: f32 [R + T][I/128] (FP8 act only) */
+  MOE_BUF_Y = 4         /* expert outputs: [R + T][H] in the output dtype; rows R.. = shared expert */
+} moe_buffer;
+
+/* Creates a context on the current HIP device and allocates all of its workspace
+ * (sized by cfg->max_tokens).  On success *out owns the context. */
+moe_status moe_create(const moe_config* cfg, moe_ctx** out);
+
+/* Frees the context and its workspace (waits for the device first). NULL is a no-op. */
+moe_status moe_destroy(moe_ctx* ctx);
+
+/*
+ * Dispatch [S sources x T_s tokens x k slots] into the windows.
+ *   tokens_per_src  T_s, 0..max_tokens (0 = nothing to do)
+ *   x               host array [S] of device pointers; x[s] -> [T_s][H] e4m3 bytes
+ *                   (or f32 for F32 act), 16-byte aligned
+ *   x_scale         host array [S] of device pointers; x_scale[s] -> f32 [T_s][H/128]
+ *                   (FP8 act); NULL for F32 act
+ *   ids             device int32 [S][T_s][k]: local expert id of each slot, -1 = not
+ *                   routed to this GPU; ids outside [-1, E) set MOE_DEVERR_BAD_ID and
+ *                   the pair is dropped
+ * The rows, counts and offsets it writes stay valid until the next dispatch.  The
+ * x buffers must stay valid until the following moe_grouped_gemm has run when a
+ * shared expert is configured (it reads them in place).
+ */
+moe_status moe_dispatch(moe_ctx* ctx, int32_t tokens_per_src, const void* const* x,
+                        const float* const* x_scale, const int32_t* ids, hipStream_t stream);
+
+/* Grouped GEMM over the windows written by the last moe_dispatch (and the shared
+ * expert over the last dispatch's x).  Experts with no rows read no weights. */
+moe_status moe_grouped_gemm(moe_ctx* ctx, const moe_weights* w, hipStream_t stream);
+
+/*
+ * Combine: out[s][t][:] = sum_j topk_w[s][t][j] * y[dst_row[s][t][j]] (+ shared y),
+ * accumulated in fp32 in slot order, for the tokens of the last dispatch.
+ *   topk_w  device f32 [S][T_s][k]
+ *   out     device [S][T_s][H] in the output dtype, 16-byte aligned
+ */
+moe_status moe_combine(moe_ctx* ctx, const float* topk_w, void* out, hipStream_t stream);
+
+/* The whole layer: dispatch, grouped GEMM and combine, synchronised per cfg.sched. */
+moe_status moe_layer(moe_ctx* ctx, int32_t tokens_per_src, const void* const* x,
+                     const float* const* x_scale, const int32_t* ids, const float* topk_w,
+                     const moe_weights* w, void* out, hipStream_t stream);
+
+/*
+ * Copies the last dispatch's control state to caller device buffers (any may be NULL):
+ *   cnt [S][E], off [S][E] (exclusive prefix of cnt[s] over e),
+ *   dst_row [S][T_s][k] (window row of each pair, -1 if not routed),
+ *   row_src [S*T_s*k] (flattened pair s*T_s*k + t*k + j filling each row, -1 if unused).
+ */
+moe_status moe_get_routing(moe_ctx* ctx, int32_t* cnt, int32_t* off, int32_t* dst_row,
+                           int32_t* row_src, hipStream_t stream);
+
+/* Copies the first `bytes` of an internal buffer to device memory `dst` (stream-ordered). */
+moe_status moe_copy_buffer(moe_ctx* ctx, moe_buffer which, void* dst, size_t bytes,
+                           hipStream_t stream);
+
+/* Waits for the device, returns the latched device error bits and clears them. */
+moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
+
+/*
+ * Per-stage timing with HIP events, for measurement.  moe_set_timing(ctx, n) keeps
+ * events for up to n moe_layer calls (0 turns timing off); moe_read_timing waits for
+ * them and returns, for the calls recorded since the last read, the summed
+ * milliseconds of [0] dispatch, [1] GEMM1 (+SwiGLU+requant), [2] GEMM2, [3] combine,
+ * [4] whole layer, and the number of calls in *n_calls.
+ */
+moe_status moe_set_timing(moe_ctx* ctx, int32_t max_calls);
+moe_status moe_read_timing(moe_ctx* ctx, float* ms_sum5, int32_t* n_calls);
+
+const char* moe_status_str(moe_status s);
+/* Detail text of the last non-OK status returned on this thread. */
+const char* moe_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CTG_MOE_H */

@@ -27,3 +27,12 @@ def lib():
         pytest.skip("no GPU")
     from combine_top_gate_amd import binding
     return binding.load()
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

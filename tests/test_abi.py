@@ -1,0 +1,74 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports every
+function include/ctg_moe.h declares, and rejects bad configurations before it
+touches the device."""
+import ctypes
+import os
+
+import pytest
+
+from combine_top_gate_amd import binding
+from conftest import gpu_available
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libctg_moe.so is not built (python -m combine_top_gate_amd.build)")
+    return binding.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = binding.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nothing declared is missing from the binding's prototypes
+    for n in ("moe_dispatch", "moe_grouped_gemm", "moe_combine", "moe_layer"):
+        assert n in names
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(1) == b"MOE_ERR_INVALID_ARG"
+    assert lib.moe_status_str(4) == b"MOE_ERR_DEVICE"
+
+
+def _create(lib, cfg):
+    ctx = ctypes.c_void_p()
+    st = lib.moe_create(ctypes.byref(cfg), ctypes.byref(ctx))
+    return st, ctx, lib.moe_last_error_message().decode()
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("hidden", 100, "hidden"), ("inter", 0, "inter"), ("n_src", 0, "n_src"),
+    ("n_src", 33, "n_src"), ("topk", 0, "topk"), ("n_experts", 300, "n_experts"),
+    ("shared_inter", 64, "shared_inter"), ("max_tokens", -1, "max_tokens"),
+    ("out", binding.MOE_F32, "dtype"), ("weight", binding.MOE_F32, "dtype"),
+    ("sched", 7, "schedule"),
+])
+def test_invalid_configs_rejected_on_host(lib, field, value, needle):
+    cfg = binding.make_config(8, 16, 7168, 2048, 32, 8)
+    setattr(cfg, field, value)
+    st, ctx, msg = _create(lib, cfg)
+    assert st == binding.MOE_ERR_INVALID_ARG
+    assert needle in msg
+    assert not ctx.value
+
+
+def test_topk_above_experts_rejected(lib):
+    cfg = binding.make_config(2, 4, 256, 128, 4, 5)
+    st, _, msg = _create(lib, cfg)
+    assert st == binding.MOE_ERR_INVALID_ARG and "topk" in msg
+
+
+def test_null_arguments(lib):
+    assert lib.moe_create(None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(None, 1, None, None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_destroy(None) == binding.MOE_OK
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device error path")
+def test_valid_config_without_device_is_hip_error(lib):
+    cfg = binding.make_config(2, 4, 256, 128, 4, 2)
+    st, ctx, msg = _create(lib, cfg)
+    assert st == binding.MOE_ERR_HIP and not ctx.value
