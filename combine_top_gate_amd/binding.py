@@ -34,9 +34,11 @@ class MoeConfig(ctypes.Structure):
                 ("dispatch_cus", ctypes.c_int32)]
 
 
+WEIGHT_FIELDS = ("w13", "s13", "w2", "s2", "sh_w13", "sh_s13", "sh_w2", "sh_s2")
+
+
 class MoeWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w13", "s13", "w2", "s2", "sh_w13", "sh_s13", "sh_w2", "sh_s2")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS] + [("packed", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -77,6 +79,8 @@ def load():
         "moe_get_routing": (st, [VP, VP, VP, VP, VP, VP]),
         "moe_copy_buffer": (st, [VP, ctypes.c_int, VP, ctypes.c_size_t, VP]),
         "moe_last_device_error": (st, [VP, P(ctypes.c_uint32)]),
+        "moe_packed_sizes": (st, [P(MoeConfig), P(ctypes.c_size_t)]),
+        "moe_pack_weights": (st, [VP, P(MoeWeights), P(MoeWeights), VP]),
         "moe_set_timing": (st, [VP, I32]),
         "moe_read_timing": (st, [VP, P(ctypes.c_float), P(I32)]),
         "moe_status_str": (ctypes.c_char_p, [st]),
@@ -122,7 +126,8 @@ class DeviceInputs:
         self.w13, self.s13, self.w2, self.s2 = up(inp.w13), up(inp.s13), up(inp.w2), up(inp.s2)
         self.sh = [up(a) for a in (inp.sh_w13, inp.sh_s13, inp.sh_w2, inp.sh_s2)]
         self.weights = MoeWeights(*[_ptr(t).value for t in
-                                    (self.w13, self.s13, self.w2, self.s2, *self.sh)])
+                                    (self.w13, self.s13, self.w2, self.s2, *self.sh)], 0)
+        self.packed = None
         out_dtype = torch.bfloat16 if inp.out == "bf16" else torch.float32
         self.out = torch.empty((inp.S, inp.T_s, inp.H), dtype=out_dtype, device=device)
 
@@ -199,6 +204,18 @@ class Moe:
         bits = ctypes.c_uint32()
         _check(self.lib.moe_last_device_error(self.ctx, ctypes.byref(bits)))
         return bits.value
+
+    def pack(self, d):
+        """Packs d's row-major weights into new device buffers; d.weights then points at them."""
+        sizes = (ctypes.c_size_t * 8)()
+        _check(self.lib.moe_packed_sizes(ctypes.byref(self.cfg), sizes))
+        bufs = [torch.empty((max(1, n),), dtype=torch.uint8, device="cuda") if n else None for n in sizes]
+        dst = MoeWeights(*[_ptr(b).value for b in bufs], 1)
+        _check(self.lib.moe_pack_weights(self.ctx, ctypes.byref(d.weights), ctypes.byref(dst), _stream()))
+        d.packed = bufs
+        d.row_major_weights = d.weights
+        d.weights = dst
+        return d
 
     def set_timing(self, max_calls):
         _check(self.lib.moe_set_timing(self.ctx, max_calls))

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "pack_layout.h"
 
 namespace {
 
@@ -105,13 +106,14 @@ moe_status check_config(const moe_config* c) {
   return MOE_OK;
 }
 
-// 16-token tiles per pass of the low-precision GEMMs: enough for a typical expert
-// (mean rows + two standard deviations of a multinomial count) in one pass.
+// Most 16-token tiles per pass of the low-precision GEMMs (each pass takes only the
+// tiles it needs): enough for a typical expert (mean rows + two standard deviations
+// of a multinomial count) in one pass, 2..4.
 int tok_tiles(const BatchDims& d) {
   const double mean = (double)d.R / d.E;
   const double want = mean + 2.0 * std::sqrt(mean);
   int nt = (int)std::ceil(want / 16.0);
-  return std::min(6, std::max(1, nt));
+  return std::min(4, std::max(2, nt));
 }
 
 void record(moe_ctx* c, int stage, hipStream_t st) {
@@ -230,6 +232,9 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   if (!w->w13 || !w->w2 || (!f32 && (!w->s13 || !w->s2)))
     return fail(MOE_ERR_INVALID_ARG, "routed expert weight or scale pointer is NULL");
   if (!aligned16(w->w13) || !aligned16(w->w2)) return fail(MOE_ERR_INVALID_ARG, "weights not 16-byte aligned");
+  if (w->packed && f32) return fail(MOE_ERR_INVALID_ARG, "F32 weights have no packed form");
+  if (w->packed && fp4 && (((uintptr_t)w->s13 | (uintptr_t)w->s2) & 3u))
+    return fail(MOE_ERR_INVALID_ARG, "packed e8m0 scales must be 4-byte aligned");
   if (cf.shared_inter) {
     if (!w->sh_w13 || !w->sh_w2 || (!f32 && (!w->sh_s13 || !w->sh_s2)))
       return fail(MOE_ERR_INVALID_ARG, "shared expert weight or scale pointer is NULL");
@@ -248,6 +253,8 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.off = c->off;
   g.src = c->src;
   g.err = c->err;
+  const bool packed = w->packed != 0;
+  const int Ish = cf.shared_inter;
   // GEMM1
   g.w = static_cast<const uint8_t*>(w->w13);
   g.ws = w->s13;
@@ -256,10 +263,10 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   if (f32) {
     g.w_stride = 2 * I * H * 4;
   } else if (fp4) {
-    g.w_stride = 2 * I * (H / 2);
-    g.ws_stride = 2 * I * (H / 32);
+    g.w_stride = packed_w13_bytes(MOE_FP4_E2M1, (int)H, (int)I);
+    g.ws_stride = packed_e13_bytes((int)H, (int)I);
   } else {
-    g.w_stride = 2 * I * H;
+    g.w_stride = packed_w13_bytes(MOE_FP8_E4M3, (int)H, (int)I);
     g.ws_stride = (2 * I / 128) * (H / 128);
   }
   g.a = c->win;
@@ -267,7 +274,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.h = c->h;
   g.hs = c->hs;
   const int nt = tok_tiles(d);
-  HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, nt, stream));
+  HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
   if (timed) record(c, 2, stream);
   // GEMM2
   g.w = static_cast<const uint8_t*>(w->w2);
@@ -277,17 +284,18 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   if (f32) {
     g.w_stride = H * I * 4;
   } else if (fp4) {
-    g.w_stride = H * (I / 2);
-    g.ws_stride = H * (I / 32);
+    g.w_stride = packed ? packed_w2_bytes(MOE_FP4_E2M1, (int)H, (int)I) : H * (I / 2);
+    g.ws_stride = packed ? packed_e2_bytes((int)H, (int)I) : H * (I / 32);
   } else {
-    g.w_stride = H * I;
+    g.w_stride = packed ? packed_w2_bytes(MOE_FP8_E4M3, (int)H, (int)I) : H * I;
     g.ws_stride = (H / 128) * (I / 128);
   }
+  (void)Ish;
   g.a = c->h;
   g.as = c->hs;
   g.y = static_cast<uint16_t*>(c->y);
   g.yf = static_cast<float*>(c->y);
-  HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, nt, stream));
+  HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
   return MOE_OK;
 }
 
@@ -362,6 +370,88 @@ moe_status moe_copy_buffer(moe_ctx* c, moe_buffer which, void* dst, size_t bytes
   if (bytes > cap) return fail(MOE_ERR_INVALID_ARG, "%zu bytes requested, buffer holds %zu", bytes, cap);
   if (bytes) HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream));
   return MOE_OK;
+}
+
+moe_status moe_packed_sizes(const moe_config* cfg, size_t sizes[8]) {
+  if (!sizes) return fail(MOE_ERR_INVALID_ARG, "sizes is NULL");
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->weight == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "F32 weights have no packed form");
+  const int H = cfg->hidden, I = cfg->inter, Ish = cfg->shared_inter;
+  const size_t E = cfg->n_experts;
+  const bool fp4 = cfg->weight == MOE_FP4_E2M1;
+  auto sc13 = [&](int inter) { return fp4 ? (size_t)packed_e13_bytes(H, inter) : (size_t)(2 * inter / 128) * (H / 128) * 4; };
+  auto sc2 = [&](int inter) { return fp4 ? (size_t)packed_e2_bytes(H, inter) : (size_t)(H / 128) * (inter / 128) * 4; };
+  sizes[0] = E * packed_w13_bytes(cfg->weight, H, I);
+  sizes[1] = E * sc13(I);
+  sizes[2] = E * packed_w2_bytes(cfg->weight, H, I);
+  sizes[3] = E * sc2(I);
+  sizes[4] = Ish ? (size_t)packed_w13_bytes(cfg->weight, H, Ish) : 0;
+  sizes[5] = Ish ? sc13(Ish) : 0;
+  sizes[6] = Ish ? (size_t)packed_w2_bytes(cfg->weight, H, Ish) : 0;
+  sizes[7] = Ish ? sc2(Ish) : 0;
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(moe_ctx* c, const moe_weights* src, const moe_weights* dst, hipStream_t stream) {
+  if (!c || !src || !dst) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  const moe_config& cf = c->cfg;
+  if (cf.weight == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "F32 weights have no packed form");
+  if (src->packed || !dst->packed) return fail(MOE_ERR_INVALID_ARG, "src must be row-major and dst packed");
+  size_t sz[8];
+  moe_status st = moe_packed_sizes(&cf, sz);
+  if (st != MOE_OK) return st;
+  const void* s8[8] = {src->w13, src->s13, src->w2, src->s2, src->sh_w13, src->sh_s13, src->sh_w2, src->sh_s2};
+  const void* d8[8] = {dst->w13, dst->s13, dst->w2, dst->s2, dst->sh_w13, dst->sh_s13, dst->sh_w2, dst->sh_s2};
+  for (int i = 0; i < 8; ++i)
+    if (sz[i] && (!s8[i] || !d8[i])) return fail(MOE_ERR_INVALID_ARG, "weight buffer %d is NULL", i);
+  for (int i = 0; i < 8; ++i)
+    if (sz[i] && (!aligned16(s8[i]) || !aligned16(d8[i])))
+      return fail(MOE_ERR_INVALID_ARG, "weight buffer %d is not 16-byte aligned", i);
+  const int H = cf.hidden, wf = cf.weight;
+  const bool fp4 = wf == MOE_FP4_E2M1;
+  auto pack_set = [&](int E, int inter, int i13, int i2) -> moe_status {
+    PackArgs a{};
+    a.E = E;
+    a.wfmt = wf;
+    // W13: [2*inter][H]
+    a.src = static_cast<const uint8_t*>(s8[i13]);
+    a.dst = static_cast<uint8_t*>(const_cast<void*>(d8[i13]));
+    a.src_stride = (int64_t)2 * inter * H / (fp4 ? 2 : 1);
+    a.dst_stride = packed_w13_bytes(wf, H, inter);
+    a.gemm1 = 1; a.K = H; a.N = 2 * inter; a.inter = inter; a.nblk = inter / 128;
+    HIP_TRY(launch_pack(a, false, stream));
+    if (fp4) {
+      a.src = static_cast<const uint8_t*>(s8[i13 + 1]);
+      a.dst = static_cast<uint8_t*>(const_cast<void*>(d8[i13 + 1]));
+      a.src_stride = (int64_t)2 * inter * (H / 32);
+      a.dst_stride = packed_e13_bytes(H, inter);
+      HIP_TRY(launch_pack(a, true, stream));
+    } else {
+      HIP_TRY(hipMemcpyAsync(const_cast<void*>(d8[i13 + 1]), s8[i13 + 1], sz[i13 + 1], hipMemcpyDeviceToDevice, stream));
+    }
+    // W2: [H][inter]
+    a.src = static_cast<const uint8_t*>(s8[i2]);
+    a.dst = static_cast<uint8_t*>(const_cast<void*>(d8[i2]));
+    a.src_stride = (int64_t)H * inter / (fp4 ? 2 : 1);
+    a.dst_stride = packed_w2_bytes(wf, H, inter);
+    a.gemm1 = 0; a.K = inter; a.N = H; a.inter = inter; a.nblk = (H + 255) / 256;
+    HIP_TRY(launch_pack(a, false, stream));
+    if (fp4) {
+      a.src = static_cast<const uint8_t*>(s8[i2 + 1]);
+      a.dst = static_cast<uint8_t*>(const_cast<void*>(d8[i2 + 1]));
+      a.src_stride = (int64_t)H * (inter / 32);
+      a.dst_stride = packed_e2_bytes(H, inter);
+      HIP_TRY(launch_pack(a, true, stream));
+    } else {
+      HIP_TRY(hipMemcpyAsync(const_cast<void*>(d8[i2 + 1]), s8[i2 + 1], sz[i2 + 1], hipMemcpyDeviceToDevice, stream));
+    }
+    return MOE_OK;
+  };
+  st = pack_set(cf.n_experts, cf.inter, 0, 2);
+  if (st != MOE_OK) return st;
+  if (cf.shared_inter) st = pack_set(1, cf.shared_inter, 4, 6);
+  return st;
 }
 
 moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {

@@ -10,14 +10,21 @@
 // requantization, optional shared experts; "One-Sided Expert-Parallel All-to-All for
 // Mixture-of-Experts Inference over NVLink", abstract: windows are read in place.)
 //
-// Decode shapes give each expert a few dozen rows against thousands of weight rows,
-// so the weights go in the MFMA's 16-row A slot and the tokens in its 16-column B
-// slot (operand swap).  Each wave streams its weight rows straight from HBM into
-// registers in the MFMA operand layout, two 128-deep K slabs ahead; the workgroup's
-// token rows (at most 16*NT of them per pass) go through LDS once per K slab and are
-// shared by the four waves.  One MFMA covers exactly one 128-wide scale block, so
-// its fp32 result is promoted with (weight scale x token scale) before it is added
-// to the accumulator.  Experts with more rows than one pass take several passes.
+// Decode shapes give an expert a few dozen rows against thousands of weight rows: the
+// layer is bound by streaming the weights from HBM once.  So the weights go in the
+// MFMA's 16-row A slot and the tokens in its 16-column B slot (operand swap), each
+// wave owns 4 tiles of 16 weight rows and streams them K slab by K slab (128 deep)
+// into registers, one slab ahead, and reads its token fragments straight from L2
+// (an expert's rows are shared by the workgroups of that expert, which all run on one
+// XCD).  Weight scales sit in lanes and token scales in LDS (staged once per pass), so
+// the K loop's only memory operations are the slab loads, and it has no barrier.  One MFMA covers exactly
+// one 128-wide scale block, so its fp32 result is promoted with (weight scale x token
+// scale) before it is added to the accumulator.
+//
+// Weights come row-major or "packed" (moe_pack_weights): packed, each wave's weights
+// are one contiguous stream in the order the wave consumes them, 1 KB per load
+// instruction -- measured on MI355X, such streams read at ~6.9 TB/s against
+// ~5.3-6.1 TB/s for 16 rows x 64 B per instruction.
 //
 // MFMA operand layout on gfx950 (16x16x128, measured): lane l serves row/column
 // l%16; with g = l/16, an FP8 operand holds k = 16g..16g+15 in bytes 0..15 and
@@ -25,19 +32,29 @@
 // nibbles (element 2i in the low nibble of byte i) and lane l's e8m0 scale covers
 // exactly those 32 k.  The result's lane l, register i is row 4g+i, column l%16.
 #include "kernels.h"
+#include "pack_layout.h"
 
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define GLOBAL __attribute__((address_space(1)))
 
-constexpr int kTokStride = 144;  // LDS bytes per staged 128-byte token slab row (+16 against bank conflicts)
+// Loads through the global address space (generic pointers would become flat loads,
+// which also count against the LDS counter).
+__device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const GLOBAL u32x4*)p; }
+__device__ __forceinline__ u32x4 gload16_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load((const GLOBAL u32x4*)p);
+}
+__device__ __forceinline__ float gloadf(const float* p) { return *(const GLOBAL float*)p; }
+__device__ __forceinline__ uint32_t gload32(const uint8_t* p) { return *(const GLOBAL uint32_t*)p; }
+__device__ __forceinline__ uint32_t gload8(const uint8_t* p) { return *(const GLOBAL uint8_t*)p; }
 
 template <int WFMT>
 struct WeightFmt;
 template <>
 struct WeightFmt<MOE_FP8_E4M3> {
-  static constexpr int kLoads = 2;  // 16-byte loads per lane per 16-row tile per K slab
-  static constexpr int kSlabBytes = 128;
+  static constexpr int kLoads = 2;       // 16-byte loads per lane per 16-row tile per K slab
+  static constexpr int kSlabBytes = 128; // bytes of one row per K slab
   static constexpr int kMfmaFmt = MFMA_FMT_FP8;
 };
 template <>
@@ -47,144 +64,150 @@ struct WeightFmt<MOE_FP4_E2M1> {
   static constexpr int kMfmaFmt = MFMA_FMT_FP4;
 };
 
-// Per-pass token table: where each of the pass's rows is read from and written to.
-template <int NTOK>
-struct TokTable {
-  const uint8_t* arow[NTOK];
-  const float* asc[NTOK];
-  int orow[NTOK];
+// Where one wave's weights (4 tiles of 16 rows) come from.
+template <int WFMT, bool PACKED>
+struct WSrc {
+  const uint8_t* row[4];   // row-major: this lane's row of each tile, + 16*g (k = 0)
+  const uint8_t* erow[4];  // row-major FP4: this lane's e8m0 bytes of each tile, + g
+  const uint8_t* base;     // packed: this wave's stream, + 16*lane
+  const uint8_t* ebase;    // packed FP4: this wave's e8m0 stream, + 4*lane
+  float fsv[2][2];         // FP8: weight scales of the tiles' two 128-row blocks, lane l
+                           //      holding K slab l (fsv[.][0]) and 64 + l (fsv[.][1])
+  int fsel[4];             // FP8: tile -> block 0 or 1
 };
 
-// Weight-side state of one wave: 4 tiles of 16 weight rows.
-template <int WFMT>
-struct WaveWeights {
-  const uint8_t* row[4];    // this lane's weight row of each tile (at k = 0)
-  const float* fscale[4];   // FP8: scale row of each tile's 128-row block, [kb]
-  const uint8_t* escale[4]; // FP4: this lane's e8m0 bytes, [kb*4]
-};
-
-template <int WFMT>
-__device__ __forceinline__ void load_w(u32x4 (&dst)[4][WeightFmt<WFMT>::kLoads],
-                                       const WaveWeights<WFMT>& ww, int kb, int g4) {
-  constexpr int SB = WeightFmt<WFMT>::kSlabBytes;
+// FP8: this wave's two weight-scale rows into lanes (KB <= 128), read back per slab with
+// v_readlane, so the K loop issues no scale loads at all.
+template <int WFMT, bool PACKED>
+__device__ __forceinline__ void load_wscales(WSrc<WFMT, PACKED>& ws, const float* row0, const float* row1, int KB) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint8_t* p = ww.row[mt] + (int64_t)kb * SB + 16 * g4;
-    dst[mt][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    if constexpr (WeightFmt<WFMT>::kLoads == 2)
-      dst[mt][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 64));
+  for (int j = 0; j < 2; ++j) {
+    const int kb = lane + 64 * j;
+    ws.fsv[0][j] = kb < KB ? row0[kb] : 0.f;
+    ws.fsv[1][j] = kb < KB ? row1[kb] : 0.f;
   }
 }
 
-// Main loop of one pass: acc[mt][nt] += promoted MFMA results over all K slabs.
-// Token rows come from tab; row_stride is the byte stride of the activation rows,
-// KB the number of 128-deep K slabs.  Every thread of the workgroup calls this.
-template <int NT, int WFMT>
-__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WaveWeights<WFMT>& ww,
-                                         const TokTable<16 * NT>& tab,
-                                         uint8_t (*s_tok)[16 * NT * kTokStride],
-                                         float (*s_tsc)[16 * NT], int KB, bool wave_active) {
-  constexpr int NTOK = 16 * NT;
-  constexpr int PIECES = NTOK * 8;  // 16-byte pieces of one token slab
-  constexpr int TLD = (PIECES + 255) / 256;
-  constexpr int WL = WeightFmt<WFMT>::kLoads;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int g4 = lane >> 4, r16 = lane & 15;
+__device__ __forceinline__ float lane_value(const float (&v)[2], int kb) {
+  const int lo = __builtin_amdgcn_readlane(__float_as_int(v[0]), kb & 63);
+  const int hi = __builtin_amdgcn_readlane(__float_as_int(v[1]), kb & 63);
+  return __int_as_float(kb < 64 ? lo : hi);
+}
 
+// One K slab of operands for one wave.
+template <int WFMT, int NT>
+struct Slab {
+  u32x4 w[4][WeightFmt<WFMT>::kLoads];
+  uint32_t e;              // FP4: e8m0 of tile mt in byte mt
+  u32x4 t[NT][2];
+};
+
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void load_slab(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws,
+                                          const uint8_t* const (&trow)[NT], int kb) {
+  constexpr int WL = WeightFmt<WFMT>::kLoads;
+  if constexpr (PACKED) {
+    const uint8_t* p = ws.base + (int64_t)kb * (4 * WL * 1024);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int h = 0; h < WL; ++h) s.w[mt][h] = gload16_nt(p + (mt * WL + h) * 1024);
+    if constexpr (WFMT == MOE_FP4_E2M1) s.e = gload32(ws.ebase + (int64_t)kb * 256);
+  } else {
+    constexpr int SB = WeightFmt<WFMT>::kSlabBytes;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint8_t* p = ws.row[mt] + (int64_t)kb * SB;
+      s.w[mt][0] = gload16_nt(p);
+      if constexpr (WL == 2) s.w[mt][1] = gload16_nt(p + 64);
+    }
+    if constexpr (WFMT == MOE_FP4_E2M1) {
+      uint32_t e = 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) e |= gload8(ws.erow[mt] + kb * 4) << (8 * mt);
+      s.e = e;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    s.t[nt][0] = gload16(trow[nt] + (int64_t)kb * 128);
+    s.t[nt][1] = gload16(trow[nt] + (int64_t)kb * 128 + 64);
+  }
+}
+
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const Slab<WFMT, NT>& s,
+                                             const WSrc<WFMT, PACKED>& ws, const float* s_tsc, int kb) {
+  float fs[2] = {1.f, 1.f};
+  if constexpr (WFMT == MOE_FP8_E4M3) {
+    fs[0] = lane_value(ws.fsv[0], kb);
+    fs[1] = lane_value(ws.fsv[1], kb);
+  }
+  const int r16 = threadIdx.x & 15;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const v8i bv = {(int)s.t[nt][0].x, (int)s.t[nt][0].y, (int)s.t[nt][0].z, (int)s.t[nt][0].w,
+                    (int)s.t[nt][1].x, (int)s.t[nt][1].y, (int)s.t[nt][1].z, (int)s.t[nt][1].w};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      v8i av;
+      if constexpr (WeightFmt<WFMT>::kLoads == 2)
+        av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w,
+                 (int)s.w[mt][1].x, (int)s.w[mt][1].y, (int)s.w[mt][1].z, (int)s.w[mt][1].w};
+      else
+        av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w, 0, 0, 0, 0};
+      const int ea = WFMT == MOE_FP4_E2M1 ? (int)((s.e >> (8 * mt)) & 0xFFu) : E8M0_ONE;
+      const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          av, bv, v4f{0.f, 0.f, 0.f, 0.f}, WeightFmt<WFMT>::kMfmaFmt, MFMA_FMT_FP8, 0, ea, 0, E8M0_ONE);
+      const float sc = (WFMT == MOE_FP8_E4M3 ? fs[ws.fsel[mt]] : 1.f) * s_tsc[kb * (16 * NT) + nt * 16 + r16];
+      acc[mt][nt][0] = fmaf(r[0], sc, acc[mt][nt][0]);
+      acc[mt][nt][1] = fmaf(r[1], sc, acc[mt][nt][1]);
+      acc[mt][nt][2] = fmaf(r[2], sc, acc[mt][nt][2]);
+      acc[mt][nt][3] = fmaf(r[3], sc, acc[mt][nt][3]);
+    }
+  }
+}
+
+// acc[mt][nt] = promoted sum over all K slabs; one slab in flight while one is consumed.
+// s_tsc holds the pass's token scales, [kb][16*NT].  The scheduling fences keep the
+// loads of the next slab ahead of the consumption of the current one, so the wait
+// before each slab's MFMAs leaves the next slab's loads in flight.
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws,
+                                         const uint8_t* const (&trow)[NT], const float* s_tsc, int KB) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 treg[TLD];
-  float tsreg = 0.f;
-  auto load_tok = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < TLD; ++i) {
-      const int q = tid + 256 * i;
-      if (q < PIECES) {
-        const uint8_t* ar = tab.arow[q >> 3];
-        treg[i] = ar ? *reinterpret_cast<const u32x4*>(ar + (int64_t)kb * 128 + (q & 7) * 16)
-                     : u32x4{0u, 0u, 0u, 0u};
-      }
+  Slab<WFMT, NT> a, b;
+  load_slab(a, ws, trow, 0);
+  for (int kb = 0; kb < KB; kb += 2) {
+    load_slab(b, ws, trow, min(kb + 1, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute_slab(acc, a, ws, s_tsc, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 1 < KB) {
+      load_slab(a, ws, trow, min(kb + 2, KB - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_slab(acc, b, ws, s_tsc, kb + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (tid < NTOK) {
-      const float* as = tab.asc[tid];
-      tsreg = as ? as[kb] : 0.f;
-    }
-  };
-  auto store_tok = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TLD; ++i) {
-      const int q = tid + 256 * i;
-      if (q < PIECES) *reinterpret_cast<u32x4*>(&s_tok[buf][(q >> 3) * kTokStride + (q & 7) * 16]) = treg[i];
-    }
-    if (tid < NTOK) s_tsc[buf][tid] = tsreg;
-  };
-
-  u32x4 wA[4][WL], wB[4][WL], wC[4][WL];
-  load_tok(0);
-  if (wave_active) {
-    load_w<WFMT>(wA, ww, 0, g4);
-    if (KB > 1) load_w<WFMT>(wB, ww, 1, g4);
   }
-  store_tok(0);
-  __syncthreads();
+}
 
-  auto step = [&](int kb, const u32x4 (&cur)[4][WL], u32x4 (&nxt)[4][WL]) {
-    if (kb + 1 < KB) load_tok(kb + 1);
-    if (wave_active) {
-      if (kb + 2 < KB) load_w<WFMT>(nxt, ww, kb + 2, g4);
-      const int buf = kb & 1;
-      float fs[4];
-      int es[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if constexpr (WFMT == MOE_FP8_E4M3) {
-          fs[mt] = ww.fscale[mt][kb];
-          es[mt] = E8M0_ONE;
-        } else {
-          fs[mt] = 1.f;
-          es[mt] = ww.escale[mt][kb * 4];
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint8_t* tp = &s_tok[buf][(nt * 16 + r16) * kTokStride + 16 * g4];
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(tp);
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(tp + 64);
-        const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                        (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        const float sx = s_tsc[buf][nt * 16 + r16];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          v8i av;
-          if constexpr (WL == 2)
-            av = v8i{(int)cur[mt][0].x, (int)cur[mt][0].y, (int)cur[mt][0].z, (int)cur[mt][0].w,
-                     (int)cur[mt][1].x, (int)cur[mt][1].y, (int)cur[mt][1].z, (int)cur[mt][1].w};
-          else
-            av = v8i{(int)cur[mt][0].x, (int)cur[mt][0].y, (int)cur[mt][0].z, (int)cur[mt][0].w,
-                     0, 0, 0, 0};
-          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av, bv, v4f{0.f, 0.f, 0.f, 0.f}, WeightFmt<WFMT>::kMfmaFmt, MFMA_FMT_FP8, 0, es[mt], 0,
-              E8M0_ONE);
-          const float sc = fs[mt] * sx;
-          acc[mt][nt][0] = fmaf(r[0], sc, acc[mt][nt][0]);
-          acc[mt][nt][1] = fmaf(r[1], sc, acc[mt][nt][1]);
-          acc[mt][nt][2] = fmaf(r[2], sc, acc[mt][nt][2]);
-          acc[mt][nt][3] = fmaf(r[3], sc, acc[mt][nt][3]);
-        }
-      }
-    }
-    if (kb + 1 < KB) store_tok((kb + 1) & 1);
-    __syncthreads();
-  };
+constexpr int kMaxKB = 128;    // K slabs: hidden and intermediate sizes up to 16384
+constexpr int kMaxTok = 4 * 16; // tokens per pass
 
-  for (int kb = 0; kb < KB; kb += 3) {
-    step(kb, wA, wC);
-    if (kb + 1 < KB) step(kb + 1, wB, wA);
-    if (kb + 2 < KB) step(kb + 2, wC, wB);
-  }
+// The pass's token scales into LDS, s_tsc[kb][nt*16 + r16] = scale of this lane's token
+// of tile nt at K slab kb; the 16 (wave, g) lane groups split the K slabs.
+template <int NT>
+__device__ __forceinline__ void stage_token_scales(float* s_tsc, const float* const (&tsc)[NT], int KB) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  for (int kb = wave * 4 + g4; kb < KB; kb += 16)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s_tsc[kb * (16 * NT) + nt * 16 + r16] = gloadf(tsc[nt] + kb);
 }
 
 // Flat work list: routed expert g has nb_r entries, then the shared expert nb_s.
@@ -207,17 +230,101 @@ __device__ __forceinline__ int group_rows(const GemmArgs& p, int g) {
   return M;
 }
 
-// ------------------------------------------------------------------ GEMM1
-template <int NT, int WFMT>
-__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
-  constexpr int NTOK = 16 * NT;
-  __shared__ __align__(16) uint8_t s_tok[2][NTOK * kTokStride];
-  __shared__ float s_tsc[2][NTOK];
-  __shared__ TokTable<NTOK> tab;
-  __shared__ float s_amax[4][NTOK];
-
+// Token rows of one pass for this lane: column r16 of each 16-token tile.  Rows past
+// the expert's end read the pass's first row (their results are not stored).
+template <int NT, bool GEMM1>
+__device__ __forceinline__ void pass_rows(const GemmArgs& p, int g, int M, int m0, const uint8_t* (&trow)[NT],
+                                          const float* (&tsc)[NT], int (&orow)[NT]) {
   const BatchDims& d = p.d;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, g4 = lane >> 4, r16 = lane & 15;
+  const bool shared = g == d.E;
+  const int seg = d.T_s * d.k;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int m = m0 + nt * 16 + r16;
+    const int mm = m < M ? m : m0;
+    int r;
+    if (GEMM1 && shared) {
+      const int s = mm / d.T_s, t = mm - s * d.T_s;
+      trow[nt] = p.src.x[s] + (int64_t)t * d.H + 16 * g4;
+      tsc[nt] = p.src.xs[s] + (int64_t)t * (d.H >> 7);
+      r = d.R + mm;
+    } else {
+      r = shared ? d.R + mm : routed_row(p.cnt, p.off, d.S, d.E, seg, g, mm);
+      if (GEMM1) {
+        trow[nt] = p.a + (int64_t)r * d.H + 16 * g4;
+        tsc[nt] = p.as + (int64_t)r * (d.H >> 7);
+      } else {
+        trow[nt] = p.a + (int64_t)r * d.hstride + 16 * g4;
+        tsc[nt] = p.as + (int64_t)r * (d.hstride >> 7);
+      }
+    }
+    orow[nt] = m < M ? r : -1;
+  }
+}
+
+// ------------------------------------------------------------------ GEMM1
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, int g, int nb,
+                                           int M, int m0, float (*s_amax)[4 * 16], float* s_tsc) {
+  const BatchDims& d = p.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const uint8_t* trow[NT];
+  const float* tsc[NT];
+  int orow[NT];
+  pass_rows<NT, true>(p, g, M, m0, trow, tsc, orow);
+  stage_token_scales<NT>(s_tsc, tsc, d.H >> 7);
+  __syncthreads();
+  v4f acc[4][NT];
+  mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, d.H >> 7);
+
+  // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
+  float hv[2][NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float mx = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = silu(acc[t][nt][i]) * acc[2 + t][nt][i];
+        hv[t][nt][i] = v;
+        mx = fmaxf(mx, fabsf(v));
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (g4 == 0) s_amax[wave][nt * 16 + r16] = mx;
+  }
+  __syncthreads();
+  // requantise: one fp32 scale per 128 columns (this workgroup's block nb) of each row
+  const int rb = nb * 128 + 32 * wave;
+  const int hsc_stride = d.hstride >> 7;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (orow[nt] < 0) continue;
+    const int tk = nt * 16 + r16;
+    const float amax = fmaxf(fmaxf(s_amax[0][tk], s_amax[1][tk]), fmaxf(s_amax[2][tk], s_amax[3][tk]));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(hv[t][nt][i] / sc, -448.0f), 448.0f);
+      *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow[nt] * d.hstride + rb + 16 * t + 4 * g4) =
+          pack4_e4m3(q[0], q[1], q[2], q[3]);
+    }
+    if (wave == 0 && g4 == 0) p.hs[(int64_t)orow[nt] * hsc_stride + nb] = sc;
+  }
+  __syncthreads();  // s_amax and s_tsc are reused by the next pass
+}
+
+template <int NTMAX, int WFMT, bool PACKED>
+__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
+  __shared__ float s_amax[4][4 * 16];
+  __shared__ float s_tsc[kMaxKB * kMaxTok];
+  const BatchDims& d = p.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   int g, nb;
   work_item(d, d.I >> 7, d.Ish >> 7, g, nb);
@@ -228,213 +335,158 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
 
   const int K = d.H, KB = K >> 7;
   constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
-  const int64_t wrow = FP4 ? (K >> 1) : K;
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
-  WaveWeights<WFMT> ww;
-  const int rb = nb * 128 + 32 * wave;  // this wave's gate rows: rb..rb+31; up rows: inter + same
-  const int rows[4] = {rb, rb + 16, inter + rb, inter + rb + 16};
+  const uint8_t* WSb = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) +
+                       (shared ? 0 : (int64_t)g * p.ws_stride * (FP4 ? 1 : 4));
+  WSrc<WFMT, PACKED> ws;
+  const int rb = nb * 128 + 32 * wave;  // this wave's gate rows rb..rb+31; up rows inter + same
+  if constexpr (PACKED) {
+    ws.base = W + pack_w13_offset(WFMT, K, nb, wave, 0) + 16 * lane;
+    if constexpr (FP4) ws.ebase = WSb + pack_e13_offset(K, nb, wave, 0) + 4 * lane;
+  } else {
+    const int64_t wrow = FP4 ? (K >> 1) : K;
+    const int rows[4] = {rb, rb + 16, inter + rb, inter + rb + 16};
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = rows[mt] + r16;
-    ww.row[mt] = W + (int64_t)row * wrow;
-    if constexpr (FP4) {
-      const uint8_t* E8 = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
-      ww.escale[mt] = E8 + (int64_t)row * (K >> 5) + g4;
-      ww.fscale[mt] = nullptr;
-    } else {
-      const float* FS = static_cast<const float*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
-      ww.fscale[mt] = FS + (int64_t)(rows[mt] >> 7) * KB;
-      ww.escale[mt] = nullptr;
+    for (int mt = 0; mt < 4; ++mt) {
+      ws.row[mt] = W + (int64_t)(rows[mt] + r16) * wrow + 16 * g4;
+      if constexpr (FP4) ws.erow[mt] = WSb + (int64_t)(rows[mt] + r16) * (K >> 5) + g4;
     }
   }
+  if constexpr (!FP4) {
+    const float* FS = reinterpret_cast<const float*>(WSb);
+    // gate rows: block nb; up rows: block I/128 + nb
+    load_wscales(ws, FS + (int64_t)nb * KB, FS + (int64_t)((inter >> 7) + nb) * KB, KB);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = mt >> 1;
+  }
 
-  const int seg = d.T_s * d.k;
-  const int hsc_stride = d.hstride >> 7;
-  for (int m0 = 0; m0 < M; m0 += NTOK) {
-    if (tid < NTOK) {
-      const int m = m0 + tid;
-      const uint8_t* ar = nullptr;
-      const float* as = nullptr;
-      int orow = -1;
-      if (m < M) {
-        if (shared) {
-          const int s = m / d.T_s, t = m - s * d.T_s;
-          ar = p.src.x[s] + (int64_t)t * K;
-          as = p.src.xs[s] + (int64_t)t * KB;
-          orow = d.R + m;
-        } else {
-          const int r = routed_row(p.cnt, p.off, d.S, d.E, seg, g, m);
-          ar = p.a + (int64_t)r * K;
-          as = p.as + (int64_t)r * KB;
-          orow = r;
-        }
-      }
-      tab.arow[tid] = ar;
-      tab.asc[tid] = as;
-      tab.orow[tid] = orow;
+  for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
+    const int nt = min(NTMAX, (M - m0 + 15) >> 4);
+    switch (nt) {
+      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
+      default: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
     }
-    __syncthreads();
-
-    v4f acc[4][NT];
-    mainloop<NT, WFMT>(acc, ww, tab, s_tok, s_tsc, KB, true);
-
-    // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
-    float hv[2][NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = silu(acc[t][nt][i]) * acc[2 + t][nt][i];
-          hv[t][nt][i] = v;
-          mx = fmaxf(mx, fabsf(v));
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (g4 == 0) s_amax[wave][nt * 16 + r16] = mx;
-    }
-    __syncthreads();
-    // requantise: one fp32 scale per 128 columns (this workgroup's block nb) of each row
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int tk = nt * 16 + r16;
-      const int orow = tab.orow[tk];
-      if (orow < 0) continue;
-      const float amax = fmaxf(fmaxf(s_amax[0][tk], s_amax[1][tk]), fmaxf(s_amax[2][tk], s_amax[3][tk]));
-      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float q[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(hv[t][nt][i] / sc, -448.0f), 448.0f);
-        const uint32_t packed = pack4_e4m3(q[0], q[1], q[2], q[3]);
-        *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow * d.hstride + rb + 16 * t + 4 * g4) = packed;
-      }
-      if (wave == 0 && g4 == 0) p.hs[(int64_t)orow * hsc_stride + nb] = sc;
-    }
-    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ GEMM2
-template <int NT, int WFMT>
-__global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
-  constexpr int NTOK = 16 * NT;
-  __shared__ __align__(16) uint8_t s_tok[2][NTOK * kTokStride];
-  __shared__ float s_tsc[2][NTOK];
-  __shared__ TokTable<NTOK> tab;
-
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, int g, int rb,
+                                           bool active, int K, int M, int m0, float* s_tsc) {
   const BatchDims& d = p.d;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const uint8_t* trow[NT];
+  const float* tsc[NT];
+  int orow[NT];
+  pass_rows<NT, false>(p, g, M, m0, trow, tsc, orow);
+  stage_token_scales<NT>(s_tsc, tsc, K >> 7);
+  __syncthreads();
+  v4f acc[4][NT];
+  if (active) mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, K >> 7);
+  __syncthreads();  // s_tsc is reused by the next pass
+  if (!active) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (orow[nt] < 0) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t lo = bf16_bits(acc[mt][nt][0]) | (bf16_bits(acc[mt][nt][1]) << 16);
+      const uint32_t hi = bf16_bits(acc[mt][nt][2]) | (bf16_bits(acc[mt][nt][3]) << 16);
+      *reinterpret_cast<uint2*>(p.y + (int64_t)orow[nt] * d.H + rb + 16 * mt + 4 * g4) = make_uint2(lo, hi);
+    }
+  }
+}
+
+template <int NTMAX, int WFMT, bool PACKED>
+__global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
+  __shared__ float s_tsc[kMaxKB * kMaxTok];
+  const BatchDims& d = p.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int nbh = (d.H + 255) >> 8;  // 256 output rows per workgroup
+  const int nbh = (d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
   work_item(d, nbh, d.Ish ? nbh : 0, g, nb);
+  const int rb0 = nb * 256 + 64 * wave;
+  const bool active = rb0 < d.H;      // a ragged last tile: such waves only help stage scales
+  const int rb = active ? rb0 : d.H - 64;
   const bool shared = g == d.E;
   const int K = shared ? d.Ish : d.I, KB = K >> 7;
   const int M = group_rows(p, g);
   if (M == 0) return;
 
   constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
-  const int64_t wrow = FP4 ? (K >> 1) : K;
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
-  const int rb = nb * 256 + 64 * wave;  // this wave's output rows rb..rb+63
-  const bool active = rb < d.H;
-  WaveWeights<WFMT> ww;
+  const uint8_t* WSb = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) +
+                       (shared ? 0 : (int64_t)g * p.ws_stride * (FP4 ? 1 : 4));
+  WSrc<WFMT, PACKED> ws;
+  if constexpr (PACKED) {
+    ws.base = W + pack_w2_offset(WFMT, K, nb, wave, 0) + 16 * lane;
+    if constexpr (FP4) ws.ebase = WSb + pack_e2_offset(K, nb, wave, 0) + 4 * lane;
+  } else {
+    const int64_t wrow = FP4 ? (K >> 1) : K;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = active ? rb + 16 * mt + r16 : 0;
-    ww.row[mt] = W + (int64_t)row * wrow;
-    if constexpr (FP4) {
-      const uint8_t* E8 = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
-      ww.escale[mt] = E8 + (int64_t)row * (K >> 5) + g4;
-      ww.fscale[mt] = nullptr;
-    } else {
-      const float* FS = static_cast<const float*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
-      ww.fscale[mt] = FS + (int64_t)((active ? rb : 0) >> 7) * KB;
-      ww.escale[mt] = nullptr;
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = rb + 16 * mt + r16;
+      ws.row[mt] = W + (int64_t)row * wrow + 16 * g4;
+      if constexpr (FP4) ws.erow[mt] = WSb + (int64_t)row * (K >> 5) + g4;
     }
   }
-
-  const int seg = d.T_s * d.k;
-  const int hsc_stride = d.hstride >> 7;
-  for (int m0 = 0; m0 < M; m0 += NTOK) {
-    if (tid < NTOK) {
-      const int m = m0 + tid;
-      const uint8_t* ar = nullptr;
-      const float* as = nullptr;
-      int orow = -1;
-      if (m < M) {
-        const int r = shared ? d.R + m : routed_row(p.cnt, p.off, d.S, d.E, seg, g, m);
-        ar = p.a + (int64_t)r * d.hstride;
-        as = p.as + (int64_t)r * hsc_stride;
-        orow = r;
-      }
-      tab.arow[tid] = ar;
-      tab.asc[tid] = as;
-      tab.orow[tid] = orow;
-    }
-    __syncthreads();
-
-    v4f acc[4][NT];
-    mainloop<NT, WFMT>(acc, ww, tab, s_tok, s_tsc, KB, active);
-
-    if (active) {
+  if constexpr (!FP4) {
+    // this wave's 64 rows sit in one 128-row scale block
+    const float* FS = reinterpret_cast<const float*>(WSb) + (int64_t)(rb >> 7) * KB;
+    load_wscales(ws, FS, FS, KB);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int orow = tab.orow[nt * 16 + r16];
-        if (orow < 0) continue;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const uint32_t lo = bf16_bits(acc[mt][nt][0]) | (bf16_bits(acc[mt][nt][1]) << 16);
-          const uint32_t hi = bf16_bits(acc[mt][nt][2]) | (bf16_bits(acc[mt][nt][3]) << 16);
-          *reinterpret_cast<uint2*>(p.y + (int64_t)orow * d.H + rb + 16 * mt + 4 * g4) = make_uint2(lo, hi);
-        }
-      }
+    for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = 0;
+  }
+
+  for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
+    const int nt = min(NTMAX, (M - m0 + 15) >> 4);
+    switch (nt) {
+      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
+      default: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
     }
-    __syncthreads();
   }
 }
 
-template <int WFMT>
+template <int WFMT, bool PACKED>
 hipError_t launch1(const GemmArgs& a, int nt, hipStream_t st) {
   const dim3 grid(a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7)), block(256);
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((k_gemm1_lowp<1, WFMT>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_gemm1_lowp<5, WFMT>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm1_lowp<6, WFMT>), grid, block, 0, st, a); break;
-  }
+  if (nt <= 2)
+    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <int WFMT>
+template <int WFMT, bool PACKED>
 hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   const int nbh = (a.d.H + 255) >> 8;
   const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh : 0)), block(256);
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((k_gemm2_lowp<1, WFMT>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_gemm2_lowp<5, WFMT>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm2_lowp<6, WFMT>), grid, block, 0, st, a); break;
-  }
+  if (nt <= 2)
+    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st) {
-  return weight_fmt == MOE_FP4_E2M1 ? launch1<MOE_FP4_E2M1>(a, tok_tiles, st)
-                                    : launch1<MOE_FP8_E4M3>(a, tok_tiles, st);
+hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {
+  if (weight_fmt == MOE_FP4_E2M1)
+    return packed ? launch1<MOE_FP4_E2M1, true>(a, tok_tiles, st) : launch1<MOE_FP4_E2M1, false>(a, tok_tiles, st);
+  return packed ? launch1<MOE_FP8_E4M3, true>(a, tok_tiles, st) : launch1<MOE_FP8_E4M3, false>(a, tok_tiles, st);
 }
 
-hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st) {
-  return weight_fmt == MOE_FP4_E2M1 ? launch2<MOE_FP4_E2M1>(a, tok_tiles, st)
-                                    : launch2<MOE_FP8_E4M3>(a, tok_tiles, st);
+hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {
+  if (weight_fmt == MOE_FP4_E2M1)
+    return packed ? launch2<MOE_FP4_E2M1, true>(a, tok_tiles, st) : launch2<MOE_FP4_E2M1, false>(a, tok_tiles, st);
+  return packed ? launch2<MOE_FP8_E4M3, true>(a, tok_tiles, st) : launch2<MOE_FP8_E4M3, false>(a, tok_tiles, st);
 }

@@ -53,11 +53,27 @@ struct GemmArgs {
   float* yf;          // GEMM2 (F32): [R+T][H]
   uint32_t* err;
 };
-// weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; tok_tiles: 16-token tiles per pass (1..6)
-hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st);
-hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int tok_tiles, hipStream_t st);
+// weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; packed: weights in the pack_layout.h order;
+// tok_tiles: most 16-token tiles per pass (2..4)
+hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
+hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
 hipError_t launch_gemm1_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_f32(const GemmArgs& a, hipStream_t st);
+
+// ---- weight repack (pack_layout.h) -----------------------------------------
+struct PackArgs {
+  const uint8_t* src;  // row-major weights (or e8m0 scales), E experts
+  uint8_t* dst;        // packed
+  int64_t src_stride, dst_stride;  // bytes per expert
+  int E;
+  int wfmt;            // MOE_FP8_E4M3 or MOE_FP4_E2M1
+  int gemm1;           // 1: W13 (2*inter rows), 0: W2 (N = H rows)
+  int K;               // contraction length (elements)
+  int N;               // rows of the source matrix
+  int inter;           // GEMM1: I of this weight set
+  int nblk;            // GEMM1: inter/128; GEMM2: ceil(H/256)
+};
+hipError_t launch_pack(const PackArgs& a, bool scales, hipStream_t st);
 
 // ---- combine ----------------------------------------------------------------
 struct CombineArgs {

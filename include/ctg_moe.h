@@ -117,10 +117,13 @@ typedef struct moe_config {
  * Rows 0..I-1 of W13[e] are the gate projection, rows I..2I-1 the up projection.
  * The shared expert (sh_*) has the same layout with E = 1 and I = shared_inter;
  * its pointers are ignored when shared_inter = 0.
+ * packed = 0: the row-major layouts above.  packed = 1: buffers written by
+ * moe_pack_weights (FP8 and MXFP4 only), the order in which the GEMM streams them.
  */
 typedef struct moe_weights {
   const void *w13, *s13, *w2, *s2;
   const void *sh_w13, *sh_s13, *sh_w2, *sh_s2;
+  int32_t packed;
 } moe_weights;
 
 typedef struct moe_ctx moe_ctx;
@@ -187,6 +190,21 @@ moe_status moe_get_routing(moe_ctx* ctx, int32_t* cnt, int32_t* off, int32_t* ds
 /* Copies the first `bytes` of an internal buffer to device memory `dst` (stream-ordered). */
 moe_status moe_copy_buffer(moe_ctx* ctx, moe_buffer which, void* dst, size_t bytes,
                            hipStream_t stream);
+
+/*
+ * Weight packing (a one-time preparation, as at model load): the grouped GEMM streams
+ * each expert's weights from HBM once per call, and streams them fastest when every
+ * wavefront's share is one contiguous run in the order it is consumed.
+ * moe_packed_sizes gives the byte size of each of the 8 moe_weights buffers of the
+ * packed form, in field order (w13, s13, w2, s2, sh_w13, sh_s13, sh_w2, sh_s2; 0 for
+ * unused fields).  moe_pack_weights rewrites the row-major set src into the caller's
+ * buffers dst (which must have those sizes, dst->packed = 1, no overlap with src);
+ * FP8 block scales are copied unchanged, MXFP4 e8m0 scales are permuted with their
+ * weights.  Stream-ordered; F32 weights return MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_packed_sizes(const moe_config* cfg, size_t sizes[8]);
+moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weights* dst,
+                            hipStream_t stream);
 
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);

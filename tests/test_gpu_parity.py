@@ -78,11 +78,13 @@ def out_np(inp, t):
     return bf16_np(t) if inp.out == "bf16" else t.cpu().numpy().astype(np.float64)
 
 
-def run(inp, moe=None, max_tokens=None):
+def run(inp, moe=None, max_tokens=None, packed=False):
     print(f"[gpu case] {inp.name} S={inp.S} T_s={inp.T_s} H={inp.H} I={inp.I} E={inp.E} "
-          f"k={inp.k} w={inp.weight} shared={inp.shared_I}", flush=True)
+          f"k={inp.k} w={inp.weight} shared={inp.shared_I} packed={packed}", flush=True)
     moe = moe or binding.Moe.for_inputs(inp, max_tokens=max_tokens)
     d = binding.DeviceInputs(inp)
+    if packed:
+        moe.pack(d)
     moe.run(d)
     torch.cuda.synchronize()
     return moe, d
@@ -121,18 +123,20 @@ def check_routing(g, ref):
 
 
 SMALL = [
-    ("tiny_f32", {}),
-    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=11)),
-    ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=12)),
-    ("prefill4096_zipf_fp8", dict(S=2, T_s=40, H=256, I=384, E=6, k=4, seed=13)),
-    ("decode128_fp8", dict(S=5, T_s=3, H=128, I=128, E=7, k=2, seed=14)),
+    ("tiny_f32", {}, False),
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=11), False),
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=11), True),
+    ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=12), False),
+    ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=12), True),
+    ("prefill4096_zipf_fp8", dict(S=2, T_s=40, H=256, I=384, E=6, k=4, seed=13), True),
+    ("decode128_fp8", dict(S=5, T_s=3, H=128, I=128, E=7, k=2, seed=14), True),
 ]
 
 
-@pytest.mark.parametrize("name,over", SMALL)
-def test_stages_match_oracle(name, over):
+@pytest.mark.parametrize("name,over,packed", SMALL)
+def test_stages_match_oracle(name, over, packed):
     inp = synth.make_inputs(name, **over)
-    moe, d = run(inp)
+    moe, d = run(inp, packed=packed)
     g = gpu_state(moe, inp)
     ref = layer.moe_layer(inp)
     check_routing(g, ref)
@@ -196,7 +200,7 @@ def _full(name):
                                   "prefill4096_zipf_fp8"])
 def test_full_size(name):
     inp = _full(name)
-    moe, d = run(inp)
+    moe, d = run(inp, packed=inp.weight != "f32")
     cnt, off, dst, src = (t.cpu().numpy() for t in moe.routing(inp.S, inp.T_s, inp.k, inp.E))
     ref = layer.dispatch(inp.ids, inp.E)
     check_routing({"cnt": cnt, "off": off, "dst_row": dst, "row_src": src}, ref)
@@ -220,6 +224,25 @@ def test_full_size(name):
         assert close(gsel, want, TOL[inp.out])
     assert np.isfinite(got).all()
     assert moe.device_error() == 0
+
+
+@pytest.mark.parametrize("name,over", [
+    ("decode128_fp8", dict(S=4, T_s=9, H=512, I=384, E=6, k=3, seed=51)),
+    ("decode256_mxfp4_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=52)),
+    ("decode128_fp8", {}),
+])
+def test_packed_weights_give_identical_output(name, over):
+    """Packing only reorders weight bytes: the GEMM sees the same operands in the same order."""
+    inp = synth.make_inputs(name, **over)
+    moe, d = run(inp)
+    ref = d.out.clone()
+    moe.pack(d)
+    d.out.zero_()
+    moe.run(d)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, d.out)
+    hb = moe.buffer(binding.MOE_BUF_H, 64)
+    assert hb.numel() == 64
 
 
 def test_empty_batch_is_noop():
