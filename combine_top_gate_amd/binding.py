@@ -21,6 +21,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = range(4)
 MOE_SCHED_FENCE, MOE_SCHED_SENTINEL = range(2)
 MOE_BUF_WINDOW, MOE_BUF_WSCALE, MOE_BUF_H, MOE_BUF_HSCALE, MOE_BUF_Y = range(5)
 MOE_DEVERR_BAD_ID, MOE_DEVERR_TIMEOUT = 0x1, 0x2
+MOE_OPT_PERSISTENT_GEMM, MOE_OPT_TOKEN_TILES, MOE_OPT_QUEUE = range(3)
 
 _DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "fp4": MOE_FP4_E2M1}
 
@@ -82,6 +83,7 @@ def load():
         "moe_packed_sizes": (st, [P(MoeConfig), P(ctypes.c_size_t)]),
         "moe_pack_weights": (st, [VP, P(MoeWeights), P(MoeWeights), VP]),
         "moe_set_timing": (st, [VP, I32]),
+        "moe_set_option": (st, [VP, ctypes.c_int, I32]),
         "moe_read_timing": (st, [VP, P(ctypes.c_float), P(I32)]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
@@ -216,6 +218,9 @@ class Moe:
         d.row_major_weights = d.weights
         d.weights = dst
         return d
+
+    def set_option(self, opt, value):
+        _check(self.lib.moe_set_option(self.ctx, opt, value))
 
     def set_timing(self, max_calls):
         _check(self.lib.moe_set_timing(self.ctx, max_calls))

@@ -29,6 +29,8 @@ moe_status fail(moe_status s, const char* fmt, ...) {
   } while (0)
 
 constexpr int kStages = 5;  // dispatch, gemm1, gemm2, combine, layer
+constexpr int kSchedWords = 16 + MOE_MAX_EXPERTS + 1 + 15;
+constexpr uint32_t kSpinLimit = 1u << 22;  // ~0.2 s of s_sleep polling
 
 }  // namespace
 
@@ -49,6 +51,10 @@ struct moe_ctx {
   int32_t* dst_row = nullptr;
   int32_t* row_src = nullptr;
   uint32_t* err = nullptr;
+  uint32_t* sched = nullptr;  // persistent GEMM: queue heads, exit count, per-group counters
+  int n_cu = 0;
+  // options
+  int opt_persistent = 0, opt_tiles = 0, opt_queue = 0;
   // state of the last dispatch
   int T_s = -1;
   SrcPtrs src{};
@@ -109,7 +115,8 @@ moe_status check_config(const moe_config* c) {
 // Most 16-token tiles per pass of the low-precision GEMMs (each pass takes only the
 // tiles it needs): enough for a typical expert (mean rows + two standard deviations
 // of a multinomial count) in one pass, 2..4.
-int tok_tiles(const BatchDims& d) {
+int tok_tiles(const BatchDims& d, int opt) {
+  if (opt) return opt;
   const double mean = (double)d.R / d.E;
   const double want = mean + 2.0 * std::sqrt(mean);
   int nt = (int)std::ceil(want / 16.0);
@@ -171,11 +178,17 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (e = alloc((void**)&c->off, (size_t)S * E * 4)) != hipSuccess ||
       (e = alloc((void**)&c->dst_row, (size_t)S * Tc * k * 4)) != hipSuccess ||
       (e = alloc((void**)&c->row_src, (size_t)c->R_cap * 4)) != hipSuccess ||
-      (e = alloc((void**)&c->err, 4)) != hipSuccess)
+      (e = alloc((void**)&c->err, 4)) != hipSuccess ||
+      (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "workspace allocation failed: %s", hipGetErrorString(e)));
   if ((e = hipMemset(c->err, 0, 4)) != hipSuccess || (e = hipMemset(c->cnt, 0, (size_t)S * E * 4)) != hipSuccess ||
+      (e = hipMemset(c->sched, 0, kSchedWords * 4)) != hipSuccess ||
       (e = hipMemset(c->off, 0, (size_t)S * E * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)));
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, c->device)) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e)));
+  c->n_cu = prop.multiProcessorCount;
   *out = c;
   return MOE_OK;
 }
@@ -184,7 +197,7 @@ moe_status moe_destroy(moe_ctx* c) {
   if (!c) return MOE_OK;
   (void)hipDeviceSynchronize();
   for (auto ev : c->ev) (void)hipEventDestroy(ev);
-  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y, c->cnt, c->off, c->dst_row, c->row_src, c->err};
+  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y, c->cnt, c->off, c->dst_row, c->row_src, c->err, c->sched};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete c;
@@ -254,7 +267,6 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.src = c->src;
   g.err = c->err;
   const bool packed = w->packed != 0;
-  const int Ish = cf.shared_inter;
   // GEMM1
   g.w = static_cast<const uint8_t*>(w->w13);
   g.ws = w->s13;
@@ -273,9 +285,12 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.as = c->wsc;
   g.h = c->h;
   g.hs = c->hs;
-  const int nt = tok_tiles(d);
-  HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
-  if (timed) record(c, 2, stream);
+  const int nt = tok_tiles(d, c->opt_tiles);
+  GemmArgs g1 = g;
+  if (f32 || !c->opt_persistent) {
+    HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
+    if (timed) record(c, 2, stream);
+  }
   // GEMM2
   g.w = static_cast<const uint8_t*>(w->w2);
   g.ws = w->s2;
@@ -290,12 +305,31 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     g.w_stride = packed ? packed_w2_bytes(MOE_FP8_E4M3, (int)H, (int)I) : H * I;
     g.ws_stride = (H / 128) * (I / 128);
   }
-  (void)Ish;
   g.a = c->h;
   g.as = c->hs;
   g.y = static_cast<uint16_t*>(c->y);
   g.yf = static_cast<float*>(c->y);
-  HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
+  if (f32 || !c->opt_persistent) {
+    HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
+    return MOE_OK;
+  }
+  ExpertsArgs ea{};
+  ea.g1 = g1;
+  ea.g2 = g;
+  ea.sched = c->sched;
+  ea.nb1_r = d.I / 128;
+  ea.nb1_s = d.Ish / 128;
+  ea.nb2 = (d.H + 255) / 256;
+  const double mean_rows = (double)d.R / d.E;
+  ea.per_xcd = c->opt_queue ? c->opt_queue == 1 : (d.E >= 16 && mean_rows <= 256.0);
+  ea.spin_limit = kSpinLimit;
+  const int groups = d.E + (d.Ish ? 1 : 0);
+  const int items = d.E * ea.nb1_r + ea.nb1_s + groups * ea.nb2;
+  const int per_cu = std::max(1, experts_lowp_blocks_per_cu(cf.weight, packed, nt));
+  int grid = std::min(items, per_cu * c->n_cu);
+  if (ea.per_xcd) grid = std::max(8, grid / 8 * 8);
+  HIP_TRY(launch_experts_lowp(ea, cf.weight, packed, nt, grid, stream));
+  if (timed) record(c, 2, stream);
   return MOE_OK;
 }
 
@@ -452,6 +486,25 @@ moe_status moe_pack_weights(moe_ctx* c, const moe_weights* src, const moe_weight
   if (st != MOE_OK) return st;
   if (cf.shared_inter) st = pack_set(1, cf.shared_inter, 4, 6);
   return st;
+}
+
+moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  switch (opt) {
+    case MOE_OPT_PERSISTENT_GEMM:
+      if (v != 0 && v != 1) break;
+      c->opt_persistent = v;
+      return MOE_OK;
+    case MOE_OPT_TOKEN_TILES:
+      if (v != 0 && (v < 2 || v > 4)) break;
+      c->opt_tiles = v;
+      return MOE_OK;
+    case MOE_OPT_QUEUE:
+      if (v < 0 || v > 2) break;
+      c->opt_queue = v;
+      return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);
 }
 
 moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {

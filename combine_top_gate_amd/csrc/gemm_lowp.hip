@@ -104,8 +104,7 @@ struct Slab {
 };
 
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void load_slab(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws,
-                                          const uint8_t* const (&trow)[NT], int kb) {
+__device__ __forceinline__ void load_slab_w(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws, int kb) {
   constexpr int WL = WeightFmt<WFMT>::kLoads;
   if constexpr (PACKED) {
     const uint8_t* p = ws.base + (int64_t)kb * (4 * WL * 1024);
@@ -129,11 +128,22 @@ __device__ __forceinline__ void load_slab(Slab<WFMT, NT>& s, const WSrc<WFMT, PA
       s.e = e;
     }
   }
+}
+
+template <int WFMT, int NT>
+__device__ __forceinline__ void load_slab_t(Slab<WFMT, NT>& s, const uint8_t* const (&trow)[NT], int kb) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     s.t[nt][0] = gload16(trow[nt] + (int64_t)kb * 128);
     s.t[nt][1] = gload16(trow[nt] + (int64_t)kb * 128 + 64);
   }
+}
+
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void load_slab(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws,
+                                          const uint8_t* const (&trow)[NT], int kb) {
+  load_slab_w(s, ws, kb);
+  load_slab_t(s, trow, kb);
 }
 
 template <int WFMT, bool PACKED, int NT>
@@ -173,15 +183,17 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const Slab<WFMT,
 // s_tsc holds the pass's token scales, [kb][16*NT].  The scheduling fences keep the
 // loads of the next slab ahead of the consumption of the current one, so the wait
 // before each slab's MFMAs leaves the next slab's loads in flight.
+// On entry, a holds the weights of slab 0 (issued by the caller ahead of its setup).
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws,
-                                         const uint8_t* const (&trow)[NT], const float* s_tsc, int KB) {
+                                         const uint8_t* const (&trow)[NT], const float* s_tsc, int KB,
+                                         Slab<WFMT, NT>& a) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-  Slab<WFMT, NT> a, b;
-  load_slab(a, ws, trow, 0);
+  Slab<WFMT, NT> b;
+  load_slab_t(a, trow, 0);
   for (int kb = 0; kb < KB; kb += 2) {
     load_slab(b, ws, trow, min(kb + 1, KB - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -223,22 +235,51 @@ __device__ __forceinline__ void work_item(const BatchDims& d, int nb_r, int nb_s
   }
 }
 
-__device__ __forceinline__ int group_rows(const GemmArgs& p, int g) {
-  if (g == p.d.E) return p.d.T;
-  int M = 0;
-  for (int s = 0; s < p.d.S; ++s) M += p.cnt[s * p.d.E + g];
-  return M;
+// Where an expert's rows live: source s's bucket holds rows pre[s] .. pre[s+1]-1 of the
+// expert window, starting at window row row0[s].  Built once per work item from one
+// parallel load per source (wave 0), so every later row lookup is an LDS read.
+struct SegTable {
+  int pre[MOE_MAX_SRC + 1];
+  int row0[MOE_MAX_SRC];
+};
+
+// Fills t for group g (all threads call; ends with a barrier); returns the group's rows.
+__device__ __forceinline__ int load_segments(const GemmArgs& p, int g, SegTable& t) {
+  const BatchDims& d = p.d;
+  if (threadIdx.x < 64 && g < d.E) {
+    const int s = threadIdx.x;
+    const int c = s < d.S ? p.cnt[s * d.E + g] : 0;
+    const int o = s < d.S ? p.off[s * d.E + g] : 0;
+    int inc = c;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int y = __shfl_up(inc, k, 64);
+      if (s >= k) inc += y;
+    }
+    if (s < d.S) {
+      t.pre[s] = inc - c;
+      t.row0[s] = s * d.T_s * d.k + o;
+    }
+    if (s == d.S - 1) t.pre[d.S] = inc;
+  }
+  __syncthreads();
+  return g < d.E ? t.pre[d.S] : d.T;
+}
+
+__device__ __forceinline__ int seg_row(const SegTable& t, int S, int m) {
+  int s = 0;
+  while (s + 1 < S && m >= t.pre[s + 1]) ++s;
+  return t.row0[s] + (m - t.pre[s]);
 }
 
 // Token rows of one pass for this lane: column r16 of each 16-token tile.  Rows past
 // the expert's end read the pass's first row (their results are not stored).
 template <int NT, bool GEMM1>
-__device__ __forceinline__ void pass_rows(const GemmArgs& p, int g, int M, int m0, const uint8_t* (&trow)[NT],
-                                          const float* (&tsc)[NT], int (&orow)[NT]) {
+__device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
+                                          const uint8_t* (&trow)[NT], const float* (&tsc)[NT], int (&orow)[NT]) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, g4 = lane >> 4, r16 = lane & 15;
   const bool shared = g == d.E;
-  const int seg = d.T_s * d.k;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int m = m0 + nt * 16 + r16;
@@ -250,7 +291,7 @@ __device__ __forceinline__ void pass_rows(const GemmArgs& p, int g, int M, int m
       tsc[nt] = p.src.xs[s] + (int64_t)t * (d.H >> 7);
       r = d.R + mm;
     } else {
-      r = shared ? d.R + mm : routed_row(p.cnt, p.off, d.S, d.E, seg, g, mm);
+      r = shared ? d.R + mm : seg_row(t, d.S, mm);
       if (GEMM1) {
         trow[nt] = p.a + (int64_t)r * d.H + 16 * g4;
         tsc[nt] = p.as + (int64_t)r * (d.H >> 7);
@@ -265,19 +306,22 @@ __device__ __forceinline__ void pass_rows(const GemmArgs& p, int g, int M, int m
 
 // ------------------------------------------------------------------ GEMM1
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, int g, int nb,
-                                           int M, int m0, float (*s_amax)[4 * 16], float* s_tsc) {
+__device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
+                                           int g, int nb, int M, int m0, float (*s_amax)[4 * 16], float* s_tsc) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const uint8_t* trow[NT];
   const float* tsc[NT];
   int orow[NT];
-  pass_rows<NT, true>(p, g, M, m0, trow, tsc, orow);
+  Slab<WFMT, NT> slab0;
+  load_slab_w(slab0, ws, 0);  // the first weight slab is in flight during the pass setup
+  __builtin_amdgcn_sched_barrier(0);
+  pass_rows<NT, true>(p, t, g, M, m0, trow, tsc, orow);
   stage_token_scales<NT>(s_tsc, tsc, d.H >> 7);
   __syncthreads();
   v4f acc[4][NT];
-  mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, d.H >> 7);
+  mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, d.H >> 7, slab0);
 
   // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
   float hv[2][NT][4];
@@ -319,18 +363,17 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
   __syncthreads();  // s_amax and s_tsc are reused by the next pass
 }
 
+// One GEMM1 work item: column block nb (128 gate + 128 up rows) of expert group g, over
+// all of the group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
-__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
-  __shared__ float s_amax[4][4 * 16];
-  __shared__ float s_tsc[kMaxKB * kMaxTok];
+__device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb, float (*s_amax)[4 * 16],
+                                           float* s_tsc, SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  int g, nb;
-  work_item(d, d.I >> 7, d.Ish >> 7, g, nb);
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
-  const int M = group_rows(p, g);
+  const int M = load_segments(p, g, seg);
   if (M == 0) return;  // no rows: no weight traffic (uniform over the workgroup)
 
   const int K = d.H, KB = K >> 7;
@@ -363,28 +406,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
   for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (M - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
-      default: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, g, nb, M, m0, s_amax, s_tsc); break;
+      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
+      default: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
     }
   }
 }
 
+template <int NTMAX, int WFMT, bool PACKED>
+__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
+  __shared__ float s_amax[4][4 * 16];
+  __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ SegTable seg;
+  int g, nb;
+  work_item(p.d, p.d.I >> 7, p.d.Ish >> 7, g, nb);
+  gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, seg);
+}
+
 // ------------------------------------------------------------------ GEMM2
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, int g, int rb,
-                                           bool active, int K, int M, int m0, float* s_tsc) {
+__device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
+                                           int g, int rb, bool active, int K, int M, int m0, float* s_tsc) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const uint8_t* trow[NT];
   const float* tsc[NT];
   int orow[NT];
-  pass_rows<NT, false>(p, g, M, m0, trow, tsc, orow);
+  Slab<WFMT, NT> slab0;
+  if (active) load_slab_w(slab0, ws, 0);  // the first weight slab is in flight during the pass setup
+  __builtin_amdgcn_sched_barrier(0);
+  pass_rows<NT, false>(p, t, g, M, m0, trow, tsc, orow);
   stage_token_scales<NT>(s_tsc, tsc, K >> 7);
   __syncthreads();
   v4f acc[4][NT];
-  if (active) mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, K >> 7);
+  if (active) mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, K >> 7, slab0);
   __syncthreads();  // s_tsc is reused by the next pass
   if (!active) return;
 #pragma unroll
@@ -399,21 +455,19 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
   }
 }
 
+// One GEMM2 work item: output rows nb*256 .. +255 of expert group g, over all of the
+// group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
-__global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
-  __shared__ float s_tsc[kMaxKB * kMaxTok];
+__device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb, float* s_tsc, SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int nbh = (d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
-  int g, nb;
-  work_item(d, nbh, d.Ish ? nbh : 0, g, nb);
   const int rb0 = nb * 256 + 64 * wave;
   const bool active = rb0 < d.H;      // a ragged last tile: such waves only help stage scales
   const int rb = active ? rb0 : d.H - 64;
   const bool shared = g == d.E;
   const int K = shared ? d.Ish : d.I, KB = K >> 7;
-  const int M = group_rows(p, g);
+  const int M = load_segments(p, g, seg);
   if (M == 0) return;
 
   constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
@@ -444,10 +498,97 @@ __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (M - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
-      default: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, g, rb, active, K, M, m0, s_tsc); break;
+      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
+      default: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
+    }
+  }
+}
+
+template <int NTMAX, int WFMT, bool PACKED>
+__global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
+  __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ SegTable seg;
+  const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
+  int g, nb;
+  work_item(p.d, nbh, p.d.Ish ? nbh : 0, g, nb);
+  gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, seg);
+}
+
+// ------------------------------------------------------------------ persistent
+// Both GEMMs in one launch.  Work items -- GEMM1 column blocks, then GEMM2 row blocks
+// -- are pulled from atomic queues: one per XCD (queue x serves the expert groups
+// g = x, x + 8, ... so an expert's token rows stay in that XCD's L2) or a single
+// queue (when experts are few or their loads very uneven).  A GEMM2 item of group g
+// first waits until all GEMM1 items of g have published their h rows (release
+// counter, agent scope).  Items are dequeued GEMM1-first, so a waited-on item has
+// always been taken by a running workgroup: no wait can deadlock.  The last
+// workgroup to leave resets the queues and counters for the next call.
+__device__ __forceinline__ int items1_of(const ExpertsArgs& a, int g) { return g < a.g1.d.E ? a.nb1_r : a.nb1_s; }
+
+// the q-th queue's groups are q, q + step, ...; returns (kind, g, nb) of entry i, kind 0 = none
+__device__ __forceinline__ int decode_item(const ExpertsArgs& a, int q, int step, int i, int& g, int& nb) {
+  const int nG = a.g1.d.E + (a.g1.d.Ish ? 1 : 0);
+  for (int gg = q; gg < nG; gg += step) {
+    const int n = items1_of(a, gg);
+    if (i < n) { g = gg; nb = i; return 1; }
+    i -= n;
+  }
+  for (int gg = q; gg < nG; gg += step) {
+    if (i < a.nb2) { g = gg; nb = i; return 2; }
+    i -= a.nb2;
+  }
+  return 0;
+}
+
+template <int NTMAX, int WFMT, bool PACKED>
+__global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
+  __shared__ float s_amax[4][4 * 16];
+  __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ int s_item, s_go;
+  __shared__ SegTable seg;
+  const int q = a.per_xcd ? (blockIdx.x & 7) : 0, step = a.per_xcd ? 8 : 1;
+  uint32_t* head = a.sched + q;
+  uint32_t* exits = a.sched + 8;
+  uint32_t* done1 = a.sched + 16;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = (int)atomicAdd(head, 1u);
+    __syncthreads();
+    const int i = s_item;
+    int g = 0, nb = 0;
+    const int kind = decode_item(a, q, step, i, g, nb);
+    if (kind == 0) break;  // uniform over the workgroup
+    if (kind == 1) {
+      gemm1_item<NTMAX, WFMT, PACKED>(a.g1, g, nb, s_amax, s_tsc, seg);
+      __syncthreads();  // every wave's h stores are done
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(done1 + g, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (threadIdx.x == 0) {
+        const uint32_t need = (uint32_t)items1_of(a, g);
+        uint32_t it = 0;
+        // poll without acquiring (an acquire invalidates caches other waves still use),
+        // then acquire once
+        while (__hip_atomic_load(done1 + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++it > a.spin_limit) break;
+          __builtin_amdgcn_s_sleep(8);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_go = it <= a.spin_limit;
+        if (!s_go) atomicOr(a.g1.err, MOE_DEVERR_TIMEOUT);
+      }
+      __syncthreads();
+      if (s_go) gemm2_item<NTMAX, WFMT, PACKED>(a.g2, g, nb, s_tsc, seg);
+    }
+    __syncthreads();  // s_item, s_go and the LDS tables are free again
+  }
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x - 1) {  // everyone else has left: reset for the next call
+      const int nG = a.g1.d.E + (a.g1.d.Ish ? 1 : 0);
+      for (int x = 0; x < 8; ++x) __hip_atomic_store(a.sched + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int gg = 0; gg < nG; ++gg) __hip_atomic_store(done1 + gg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(exits, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -477,7 +618,48 @@ hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int WFMT, bool PACKED>
+hipError_t launch_experts(const ExpertsArgs& a, int nt, int grid, hipStream_t st) {
+  if (nt <= 2)
+    hipLaunchKernelGGL((k_experts_lowp<2, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((k_experts_lowp<3, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_experts_lowp<4, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WFMT, bool PACKED>
+int experts_blocks_per_cu(int nt) {
+  int n = 0;
+  hipError_t e;
+  if (nt <= 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<2, WFMT, PACKED>, 256, 0);
+  else if (nt == 3)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<3, WFMT, PACKED>, 256, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<4, WFMT, PACKED>, 256, 0);
+  return e == hipSuccess ? n : 0;
+}
+
 }  // namespace
+
+hipError_t launch_experts_lowp(const ExpertsArgs& a, int weight_fmt, int packed, int tok_tiles, int grid,
+                               hipStream_t st) {
+  if (weight_fmt == MOE_FP4_E2M1)
+    return packed ? launch_experts<MOE_FP4_E2M1, true>(a, tok_tiles, grid, st)
+                  : launch_experts<MOE_FP4_E2M1, false>(a, tok_tiles, grid, st);
+  return packed ? launch_experts<MOE_FP8_E4M3, true>(a, tok_tiles, grid, st)
+                : launch_experts<MOE_FP8_E4M3, false>(a, tok_tiles, grid, st);
+}
+
+int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles) {
+  if (weight_fmt == MOE_FP4_E2M1)
+    return packed ? experts_blocks_per_cu<MOE_FP4_E2M1, true>(tok_tiles)
+                  : experts_blocks_per_cu<MOE_FP4_E2M1, false>(tok_tiles);
+  return packed ? experts_blocks_per_cu<MOE_FP8_E4M3, true>(tok_tiles)
+                : experts_blocks_per_cu<MOE_FP8_E4M3, false>(tok_tiles);
+}
 
 hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {
   if (weight_fmt == MOE_FP4_E2M1)

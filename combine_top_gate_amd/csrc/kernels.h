@@ -57,6 +57,18 @@ struct GemmArgs {
 // tok_tiles: most 16-token tiles per pass (2..4)
 hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
 hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
+// Both low-precision GEMMs in one persistent launch (work queues, see gemm_lowp.hip).
+struct ExpertsArgs {
+  GemmArgs g1, g2;
+  uint32_t* sched;      // [0..7] queue heads, [8] exit count, [16 + g] finished GEMM1 items of group g
+  int nb1_r, nb1_s;     // GEMM1 items of a routed / the shared group
+  int nb2;              // GEMM2 items of any group
+  int per_xcd;          // 1: eight queues, one per XCD; 0: one queue
+  uint32_t spin_limit;  // bound of the wait for a group's GEMM1 items
+};
+hipError_t launch_experts_lowp(const ExpertsArgs& a, int weight_fmt, int packed, int tok_tiles, int grid,
+                               hipStream_t st);
+int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles);
 hipError_t launch_gemm1_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_f32(const GemmArgs& a, hipStream_t st);
 

@@ -206,6 +206,20 @@ moe_status moe_packed_sizes(const moe_config* cfg, size_t sizes[8]);
 moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weights* dst,
                             hipStream_t stream);
 
+/*
+ * Tuning options of a context (each defaults to automatic):
+ *   MOE_OPT_PERSISTENT_GEMM  0: two kernels, one workgroup per work item (default);
+ *                            1: both GEMMs in one persistent kernel fed by work queues,
+ *                            GEMM2 items waiting on per-expert counters (the cross-XCD
+ *                            hand-off of h costs an L2 write-back per item).
+ *   MOE_OPT_TOKEN_TILES      0: automatic; 2..4: most 16-row token tiles per GEMM pass.
+ *   MOE_OPT_QUEUE            0: automatic; 1: one work queue per XCD (an expert's items
+ *                            stay on one XCD); 2: one queue for the whole GPU.
+ * Unknown options or values return MOE_ERR_INVALID_ARG.
+ */
+typedef enum { MOE_OPT_PERSISTENT_GEMM = 0, MOE_OPT_TOKEN_TILES = 1, MOE_OPT_QUEUE = 2 } moe_option;
+moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
+
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 
@@ -214,7 +228,8 @@ moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
  * events for up to n moe_layer calls (0 turns timing off); moe_read_timing waits for
  * them and returns, for the calls recorded since the last read, the summed
  * milliseconds of [0] dispatch, [1] GEMM1 (+SwiGLU+requant), [2] GEMM2, [3] combine,
- * [4] whole layer, and the number of calls in *n_calls.
+ * [4] whole layer, and the number of calls in *n_calls.  With the persistent GEMM
+ * kernel, [1] holds both GEMMs and [2] is 0.
  */
 moe_status moe_set_timing(moe_ctx* ctx, int32_t max_calls);
 moe_status moe_read_timing(moe_ctx* ctx, float* ms_sum5, int32_t* n_calls);

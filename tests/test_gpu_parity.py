@@ -245,6 +245,50 @@ def test_packed_weights_give_identical_output(name, over):
     assert hb.numel() == 64
 
 
+@pytest.mark.parametrize("name,over", [
+    ("decode128_fp8", {}),
+    ("decode256_mxfp4_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=53)),
+    ("prefill4096_zipf_fp8", dict(S=4, T_s=64, H=512, I=256, E=16, k=4, seed=54)),
+])
+def test_gemm_schedules_give_identical_output(name, over):
+    """Persistent queues (per XCD or global), separate kernels and any token tiling run
+    the same MFMAs per output element: results must agree bit for bit."""
+    inp = synth.make_inputs(name, **over)
+    moe, d = run(inp, packed=True)
+    ref = d.out.clone()
+    for opt, val in [(binding.MOE_OPT_QUEUE, 2), (binding.MOE_OPT_QUEUE, 1), (binding.MOE_OPT_TOKEN_TILES, 2),
+                     (binding.MOE_OPT_TOKEN_TILES, 4), (binding.MOE_OPT_PERSISTENT_GEMM, 0)]:
+        moe.set_option(opt, val)
+        d.out.zero_()
+        moe.run(d)
+        torch.cuda.synchronize()
+        assert torch.equal(ref, d.out), (opt, val)
+    assert moe.device_error() == 0
+
+
+def test_many_back_to_back_calls_reuse_scheduler_state():
+    """The persistent GEMM resets its queues and counters itself: 60 calls, no clean pass."""
+    inp = synth.make_inputs("decode128_fp8", S=8, T_s=4, H=1024, I=512, E=32, k=4, seed=55)
+    moe, d = run(inp, packed=True)
+    ref = d.out.clone()
+    outs = []
+    for _ in range(60):
+        moe.run(d)
+        outs.append(d.out.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(ref, o) for o in outs)
+    assert moe.device_error() == 0
+
+
+def test_invalid_options():
+    inp = synth.make_inputs("decode128_fp8", S=2, T_s=2, H=128, I=128, E=4, k=2)
+    moe = binding.Moe.for_inputs(inp)
+    for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 5), (binding.MOE_OPT_QUEUE, 3),
+                     (binding.MOE_OPT_PERSISTENT_GEMM, 2), (9, 0)]:
+        with pytest.raises(binding.MoeError):
+            moe.set_option(opt, val)
+
+
 def test_empty_batch_is_noop():
     inp = synth.make_inputs("decode128_fp8", S=2, T_s=0, H=128, I=128, E=4, k=2)
     moe = binding.Moe.for_inputs(inp, max_tokens=4)
