@@ -115,12 +115,12 @@ moe_status check_config(const moe_config* c) {
 // Most 16-token tiles per pass of the low-precision GEMMs (each pass takes only the
 // tiles it needs): enough for a typical expert (mean rows + two standard deviations
 // of a multinomial count) in one pass, 2..4.
-int tok_tiles(const BatchDims& d, int opt) {
+int tok_tiles(const BatchDims& d, int opt, bool fp4) {
   if (opt) return opt;
   const double mean = (double)d.R / d.E;
   const double want = mean + 2.0 * std::sqrt(mean);
   int nt = (int)std::ceil(want / 16.0);
-  return std::min(4, std::max(2, nt));
+  return std::min(fp4 ? 5 : 4, std::max(2, nt));
 }
 
 void record(moe_ctx* c, int stage, hipStream_t st) {
@@ -285,7 +285,10 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.as = c->wsc;
   g.h = c->h;
   g.hs = c->hs;
-  const int nt = tok_tiles(d, c->opt_tiles);
+  const int nt = tok_tiles(d, c->opt_tiles, fp4);
+  // the shared expert (all T rows): chunks of at most one pass each, as separate work items
+  g.sh_chunk_rows = 16 * nt;
+  g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
   GemmArgs g1 = g;
   if (f32 || !c->opt_persistent) {
     HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
@@ -324,7 +327,8 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   ea.per_xcd = c->opt_queue ? c->opt_queue == 1 : (d.E >= 16 && mean_rows <= 256.0);
   ea.spin_limit = kSpinLimit;
   const int groups = d.E + (d.Ish ? 1 : 0);
-  const int items = d.E * ea.nb1_r + ea.nb1_s + groups * ea.nb2;
+  const int items = d.E * ea.nb1_r + ea.nb1_s * g.sh_chunks + d.E * ea.nb2 + (d.Ish ? ea.nb2 * g.sh_chunks : 0);
+  (void)groups;
   const int per_cu = std::max(1, experts_lowp_blocks_per_cu(cf.weight, packed, nt));
   int grid = std::min(items, per_cu * c->n_cu);
   if (ea.per_xcd) grid = std::max(8, grid / 8 * 8);
@@ -496,7 +500,7 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
       c->opt_persistent = v;
       return MOE_OK;
     case MOE_OPT_TOKEN_TILES:
-      if (v != 0 && (v < 2 || v > 4)) break;
+      if (v != 0 && (v < 2 || v > 6)) break;
       c->opt_tiles = v;
       return MOE_OK;
     case MOE_OPT_QUEUE:

@@ -209,7 +209,7 @@ __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PAC
 }
 
 constexpr int kMaxKB = 128;    // K slabs: hidden and intermediate sizes up to 16384
-constexpr int kMaxTok = 4 * 16; // tokens per pass
+constexpr int kMaxTok = 6 * 16; // tokens per pass
 
 // The pass's token scales into LDS, s_tsc[kb][nt*16 + r16] = scale of this lane's token
 // of tile nt at K slab kb; the 16 (wave, g) lane groups split the K slabs.
@@ -307,7 +307,7 @@ __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, 
 // ------------------------------------------------------------------ GEMM1
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
-                                           int g, int nb, int M, int m0, float (*s_amax)[4 * 16], float* s_tsc) {
+                                           int g, int nb, int M, int m0, float (*s_amax)[kMaxTok], float* s_tsc) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -366,14 +366,23 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
 // One GEMM1 work item: column block nb (128 gate + 128 up rows) of expert group g, over
 // all of the group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
-__device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb, float (*s_amax)[4 * 16],
+__device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item, float (*s_amax)[kMaxTok],
                                            float* s_tsc, SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
+  int nb = nb_item;
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
   const int M = load_segments(p, g, seg);
+  // the shared expert's rows are split into chunks, each its own work item
+  int mb = 0, me = M;
+  if (shared) {
+    const int chunk = nb % p.sh_chunks;
+    nb /= p.sh_chunks;
+    mb = chunk * p.sh_chunk_rows;
+    me = min(M, mb + p.sh_chunk_rows);
+  }
   if (M == 0) return;  // no rows: no weight traffic (uniform over the workgroup)
 
   const int K = d.H, KB = K >> 7;
@@ -403,24 +412,26 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb, flo
     for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = mt >> 1;
   }
 
-  for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
-    const int nt = min(NTMAX, (M - m0 + 15) >> 4);
+  for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
+    const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
-      default: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, M, m0, s_amax, s_tsc); break;
+      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      case 5: if constexpr (NTMAX >= 5) gemm1_pass<WFMT, PACKED, 5>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      default: if constexpr (NTMAX >= 6) gemm1_pass<WFMT, PACKED, 6>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
     }
   }
 }
 
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
-  __shared__ float s_amax[4][4 * 16];
+  __shared__ float s_amax[4][kMaxTok];
   __shared__ float s_tsc[kMaxKB * kMaxTok];
   __shared__ SegTable seg;
   int g, nb;
-  work_item(p.d, p.d.I >> 7, p.d.Ish >> 7, g, nb);
+  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, g, nb);
   gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, seg);
 }
 
@@ -458,10 +469,15 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
 // One GEMM2 work item: output rows nb*256 .. +255 of expert group g, over all of the
 // group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
-__device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb, float* s_tsc, SegTable& seg) {
+__device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item, float* s_tsc, SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
+  int nb = nb_item, chunk = 0;
+  if (g == d.E) {  // the shared expert's rows are split into chunks, each its own work item
+    chunk = nb % p.sh_chunks;
+    nb /= p.sh_chunks;
+  }
   const int rb0 = nb * 256 + 64 * wave;
   const bool active = rb0 < d.H;      // a ragged last tile: such waves only help stage scales
   const int rb = active ? rb0 : d.H - 64;
@@ -469,6 +485,8 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb, flo
   const int K = shared ? d.Ish : d.I, KB = K >> 7;
   const int M = load_segments(p, g, seg);
   if (M == 0) return;
+  const int mb = g == d.E ? chunk * p.sh_chunk_rows : 0;
+  const int me = g == d.E ? min(M, mb + p.sh_chunk_rows) : M;
 
   constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
@@ -495,13 +513,15 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb, flo
     for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = 0;
   }
 
-  for (int m0 = 0; m0 < M; m0 += 16 * NTMAX) {
-    const int nt = min(NTMAX, (M - m0 + 15) >> 4);
+  for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
+    const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
-      default: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, M, m0, s_tsc); break;
+      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      case 4: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      case 5: if constexpr (NTMAX >= 5) gemm2_pass<WFMT, PACKED, 5>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      default: if constexpr (NTMAX >= 6) gemm2_pass<WFMT, PACKED, 6>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
     }
   }
 }
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   __shared__ SegTable seg;
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
-  work_item(p.d, nbh, p.d.Ish ? nbh : 0, g, nb);
+  work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, g, nb);
   gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, seg);
 }
 
@@ -525,7 +545,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
 // counter, agent scope).  Items are dequeued GEMM1-first, so a waited-on item has
 // always been taken by a running workgroup: no wait can deadlock.  The last
 // workgroup to leave resets the queues and counters for the next call.
-__device__ __forceinline__ int items1_of(const ExpertsArgs& a, int g) { return g < a.g1.d.E ? a.nb1_r : a.nb1_s; }
+__device__ __forceinline__ int items1_of(const ExpertsArgs& a, int g) {
+  return g < a.g1.d.E ? a.nb1_r : a.nb1_s * a.g1.sh_chunks;
+}
+__device__ __forceinline__ int items2_of(const ExpertsArgs& a, int g) {
+  return g < a.g1.d.E ? a.nb2 : a.nb2 * a.g1.sh_chunks;
+}
 
 // the q-th queue's groups are q, q + step, ...; returns (kind, g, nb) of entry i, kind 0 = none
 __device__ __forceinline__ int decode_item(const ExpertsArgs& a, int q, int step, int i, int& g, int& nb) {
@@ -536,15 +561,16 @@ __device__ __forceinline__ int decode_item(const ExpertsArgs& a, int q, int step
     i -= n;
   }
   for (int gg = q; gg < nG; gg += step) {
-    if (i < a.nb2) { g = gg; nb = i; return 2; }
-    i -= a.nb2;
+    const int n = items2_of(a, gg);
+    if (i < n) { g = gg; nb = i; return 2; }
+    i -= n;
   }
   return 0;
 }
 
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
-  __shared__ float s_amax[4][4 * 16];
+  __shared__ float s_amax[4][kMaxTok];
   __shared__ float s_tsc[kMaxKB * kMaxTok];
   __shared__ int s_item, s_go;
   __shared__ SegTable seg;
@@ -595,26 +621,30 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
 
 template <int WFMT, bool PACKED>
 hipError_t launch1(const GemmArgs& a, int nt, hipStream_t st) {
-  const dim3 grid(a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7)), block(256);
+  const dim3 grid(a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
   if (nt <= 2)
     hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
   else if (nt == 3)
     hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
-  else
+  else if (nt == 4 || WFMT != MOE_FP4_E2M1)
     hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <int WFMT, bool PACKED>
 hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   const int nbh = (a.d.H + 255) >> 8;
-  const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh : 0)), block(256);
+  const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh * a.sh_chunks : 0)), block(256);
   if (nt <= 2)
     hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
   else if (nt == 3)
     hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
-  else
+  else if (nt == 4 || WFMT != MOE_FP4_E2M1)
     hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm2_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

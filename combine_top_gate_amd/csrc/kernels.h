@@ -52,6 +52,8 @@ struct GemmArgs {
   uint16_t* y;        // GEMM2 (bf16): [R+T][H]
   float* yf;          // GEMM2 (F32): [R+T][H]
   uint32_t* err;
+  int sh_chunks;      // the shared expert's rows are split into this many work items
+  int sh_chunk_rows;  // rows per chunk (multiple of 16)
 };
 // weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; packed: weights in the pack_layout.h order;
 // tok_tiles: most 16-token tiles per pass (2..4)

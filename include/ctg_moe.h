@@ -212,7 +212,8 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *                            1: both GEMMs in one persistent kernel fed by work queues,
  *                            GEMM2 items waiting on per-expert counters (the cross-XCD
  *                            hand-off of h costs an L2 write-back per item).
- *   MOE_OPT_TOKEN_TILES      0: automatic; 2..4: most 16-row token tiles per GEMM pass.
+ *   MOE_OPT_TOKEN_TILES      0: automatic; 2..6: most 16-row token tiles per GEMM pass
+ *                            (kernels take at most 4 for FP8 and 5 for MXFP4 weights).
  *   MOE_OPT_QUEUE            0: automatic; 1: one work queue per XCD (an expert's items
  *                            stay on one XCD); 2: one queue for the whole GPU.
  * Unknown options or values return MOE_ERR_INVALID_ARG.

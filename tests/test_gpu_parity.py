@@ -283,7 +283,7 @@ def test_many_back_to_back_calls_reuse_scheduler_state():
 def test_invalid_options():
     inp = synth.make_inputs("decode128_fp8", S=2, T_s=2, H=128, I=128, E=4, k=2)
     moe = binding.Moe.for_inputs(inp)
-    for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 5), (binding.MOE_OPT_QUEUE, 3),
+    for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 7), (binding.MOE_OPT_QUEUE, 3),
                      (binding.MOE_OPT_PERSISTENT_GEMM, 2), (9, 0)]:
         with pytest.raises(binding.MoeError):
             moe.set_option(opt, val)
