@@ -31,6 +31,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 constexpr int kStages = 5;  // dispatch, gemm1, gemm2, combine, layer
 constexpr int kSchedWords = 16 + MOE_MAX_EXPERTS + 1 + 15;
 constexpr uint32_t kSpinLimit = 1u << 22;  // ~0.2 s of s_sleep polling
+constexpr double kTiledRows = 192.0;       // mean rows per expert from which the tiled GEMM runs
 
 }  // namespace
 
@@ -52,9 +53,10 @@ struct moe_ctx {
   int32_t* row_src = nullptr;
   uint32_t* err = nullptr;
   uint32_t* sched = nullptr;  // persistent GEMM: queue heads, exit count, per-group counters
+  int* plan = nullptr;        // tiled GEMM: tile table and work counters
   int n_cu = 0;
   // options
-  int opt_persistent = 0, opt_tiles = 0, opt_queue = 0;
+  int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0;
   // state of the last dispatch
   int T_s = -1;
   SrcPtrs src{};
@@ -179,7 +181,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (e = alloc((void**)&c->dst_row, (size_t)S * Tc * k * 4)) != hipSuccess ||
       (e = alloc((void**)&c->row_src, (size_t)c->R_cap * 4)) != hipSuccess ||
       (e = alloc((void**)&c->err, 4)) != hipSuccess ||
-      (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess)
+      (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->plan, (size_t)tiled_plan_words() * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "workspace allocation failed: %s", hipGetErrorString(e)));
   if ((e = hipMemset(c->err, 0, 4)) != hipSuccess || (e = hipMemset(c->cnt, 0, (size_t)S * E * 4)) != hipSuccess ||
       (e = hipMemset(c->sched, 0, kSchedWords * 4)) != hipSuccess ||
@@ -197,7 +200,8 @@ moe_status moe_destroy(moe_ctx* c) {
   if (!c) return MOE_OK;
   (void)hipDeviceSynchronize();
   for (auto ev : c->ev) (void)hipEventDestroy(ev);
-  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y, c->cnt, c->off, c->dst_row, c->row_src, c->err, c->sched};
+  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y,     c->cnt,   c->off,
+                  c->dst_row, c->row_src, c->err, c->sched, c->plan};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete c;
@@ -290,7 +294,10 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.sh_chunk_rows = 16 * nt;
   g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
   GemmArgs g1 = g;
-  if (f32 || !c->opt_persistent) {
+  // many rows per expert: the LDS-tiled, MFMA-bound kernels (FP8 weights)
+  const double rows_per_expert = (double)d.R / d.E;
+  const bool tiled = !f32 && !fp4 && (c->opt_tiled == 1 || (c->opt_tiled == 0 && rows_per_expert >= kTiledRows));
+  if (!tiled && (f32 || !c->opt_persistent)) {
     HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
     if (timed) record(c, 2, stream);
   }
@@ -312,6 +319,19 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.as = c->hs;
   g.y = static_cast<uint16_t*>(c->y);
   g.yf = static_cast<float*>(c->y);
+  if (tiled) {
+    TiledArgs ta{};
+    ta.g1 = g1;
+    ta.g2 = g;
+    ta.plan = c->plan;
+    ta.nb1_r = d.I / 128;
+    ta.nb1_s = d.Ish / 128;
+    ta.nb2 = (d.H + 255) / 256;
+    ta.packed = packed;
+    HIP_TRY(launch_tiled(ta, c->n_cu, stream));
+    if (timed) record(c, 2, stream);
+    return MOE_OK;
+  }
   if (f32 || !c->opt_persistent) {
     HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
     return MOE_OK;
@@ -506,6 +526,10 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
     case MOE_OPT_QUEUE:
       if (v < 0 || v > 2) break;
       c->opt_queue = v;
+      return MOE_OK;
+    case MOE_OPT_TILED_GEMM:
+      if (v < 0 || v > 2) break;
+      c->opt_tiled = v;
       return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);

@@ -71,6 +71,17 @@ struct ExpertsArgs {
 hipError_t launch_experts_lowp(const ExpertsArgs& a, int weight_fmt, int packed, int tok_tiles, int grid,
                                hipStream_t st);
 int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles);
+// LDS-tiled GEMMs for large expert row counts (FP8 weights; gemm_tiled.hip): a plan
+// kernel, then GEMM1 and GEMM2 on persistent grids fed by atomic work counters.
+struct TiledArgs {
+  GemmArgs g1, g2;
+  int* plan;           // tiled_plan_words() ints of workspace
+  int nb1_r, nb1_s;    // GEMM1 column blocks (128 gate + 128 up) of a routed / the shared group
+  int nb2;             // GEMM2 row blocks of 256
+  int packed;          // weights in the pack_layout.h order
+};
+hipError_t launch_tiled(const TiledArgs& a, int grid, hipStream_t st);
+int tiled_plan_words();
 hipError_t launch_gemm1_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_f32(const GemmArgs& a, hipStream_t st);
 

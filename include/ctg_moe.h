@@ -216,9 +216,17 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *                            (kernels take at most 4 for FP8 and 5 for MXFP4 weights).
  *   MOE_OPT_QUEUE            0: automatic; 1: one work queue per XCD (an expert's items
  *                            stay on one XCD); 2: one queue for the whole GPU.
+ *   MOE_OPT_TILED_GEMM       0: automatic (LDS-tiled MFMA kernels from 192 mean rows per
+ *                            expert, FP8 weights); 1: always tiled (FP8 weights);
+ *                            2: never (the weight-streaming kernels).
  * Unknown options or values return MOE_ERR_INVALID_ARG.
  */
-typedef enum { MOE_OPT_PERSISTENT_GEMM = 0, MOE_OPT_TOKEN_TILES = 1, MOE_OPT_QUEUE = 2 } moe_option;
+typedef enum {
+  MOE_OPT_PERSISTENT_GEMM = 0,
+  MOE_OPT_TOKEN_TILES = 1,
+  MOE_OPT_QUEUE = 2,
+  MOE_OPT_TILED_GEMM = 3
+} moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 
 /* Waits for the device, returns the latched device error bits and clears them. */

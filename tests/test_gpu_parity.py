@@ -16,6 +16,17 @@ its output by 1-2.5% in the elementwise statistic, so that statistic cannot hold
 2e-2 for any accumulation order but the oracle's; the row-wise error stays near
 5e-3 and the elementwise guard still catches a wrong element.
 
+Window rows y (one expert's output, before the top-k weighting) are checked the
+same way, with one addition.  An h code may legitimately differ from the oracle's
+where the exact SwiGLU value lies within fp32 accumulation error of an e4m3
+rounding midpoint: the pages fix no accumulation order inside the FP8 block
+GEMM, so both roundings are results of the method.  fp8_requant_check() takes
+that error bound from the oracle's own fp64 values (Higham's gamma_n for n fp32
+roundings times the sum of |terms|), requires every GPU code to be a correct
+rounding of some value inside that band, and widens each y row's bound by the
+oracle-computed effect of the codes that differ.  With I = 256 a single such code
+moves its row by up to 3%, against 2e-2.
+
 Small shapes span several workgroup tiles, ragged tails and multi-pass experts;
 the five full-size configurations are checked bit-exactly on the routing and on
 every token (on a sample of 48 tokens for the 4096-token one).
@@ -65,6 +76,87 @@ def close(g, r, tol):
     frac = float(np.mean(e > tol))
     print(f"  row relL2 max {row.max():.3e} | elementwise max {e.max():.3e}, frac>tol {frac:.2e}",
           flush=True)
+    return row.max() <= tol and e.max() <= 5 * tol and frac <= 1e-3
+
+
+U32 = 2.0 ** -24
+
+
+def fp8_requant_check(inp, x_rows, w13, w2, inter, ref_codes, ref_scales, g_codes, g_scales):
+    """Checks requantised SwiGLU codes against the oracle's error band; returns the
+    y-row allowance (fp64 [M]) that the legitimate code differences explain.
+
+    x_rows: dequantised activations [M][H] (oracle); w13/w2: dequantised weights
+    (oracle); ref_*: the oracle's codes and scales; g_*: the GPU's.
+    Error model: every GEMM1 output is an fp32 dot product over H terms formed as
+    128-deep block sums promoted once per block, then SwiGLU and one division;
+    n = 128 + 2 H/128 + 8 roundings in all, so |error| <= gamma_n * sum|terms|
+    (plus gamma_n |h| for the elementwise steps).
+    """
+    H = x_rows.shape[1]
+    n = 128 + 2 * (H // 128) + 8
+    gam = n * U32 / (1 - n * U32)
+    a = x_rows @ w13.T
+    mag = np.abs(x_rows) @ np.abs(w13).T
+    g, u = a[:, :inter], a[:, inter:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sg
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    h = silu * u
+    band = gam * (np.abs(dsilu * u) * mag[:, :inter] + np.abs(silu) * mag[:, inter:] + np.abs(h))
+    M = h.shape[0]
+    s = np.repeat(ref_scales, 128, axis=1)
+    # the GPU's scale may differ by the band of its block's largest element
+    ds = np.zeros_like(ref_scales)
+    for b in range(inter // 128):
+        am = np.argmax(np.abs(h[:, b * 128:(b + 1) * 128]), axis=1) + b * 128
+        amax = np.abs(h[np.arange(M), am])
+        ds[:, b] = np.where(amax > 0, band[np.arange(M), am] / np.where(amax > 0, amax, 1.0), 0.0)
+    v = h / s
+    dv = band / s + np.abs(v) * (np.repeat(ds, 128, axis=1) + 4 * U32)
+    lo = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(v - dv, -448.0, 448.0)))
+    hi = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(v + dv, -448.0, 448.0)))
+    gv = codecs.e4m3_decode(g_codes)
+    rv = codecs.e4m3_decode(ref_codes)
+    bad = (gv < lo) | (gv > hi)
+    assert not bad.any(), f"{int(bad.sum())} h codes outside the fp32 accumulation band"
+    assert np.all(np.abs(g_scales - ref_scales) <= ref_scales * (ds + 4 * U32)), "h scale outside band"
+    col = np.linalg.norm(w2, axis=0)                        # ||w2[:, i]||
+    return (np.abs(gv - rv) * s) @ col
+
+
+def window_allowance(inp, ref, g, rows_used):
+    """fp8_requant_check over every used window row, expert by expert."""
+    R = inp.S * inp.T_s * inp.k
+    xt = layer.dequant_act_fp8(np.asarray(inp.x).reshape(inp.S * inp.T_s, inp.H),
+                               np.asarray(inp.x_scale).reshape(inp.S * inp.T_s, inp.H // 128))
+    allow = np.zeros(R)
+    for e, r in enumerate(ref["expert_rows"]):
+        if len(r) == 0:
+            continue
+        w13 = layer.dequant_weight(inp.weight, inp.w13[e], None if inp.s13 is None else inp.s13[e])
+        w2 = layer.dequant_weight(inp.weight, inp.w2[e], None if inp.s2 is None else inp.s2[e])
+        allow[r] = fp8_requant_check(inp, xt[ref["row_src"][r] // inp.k], w13, w2, inp.I,
+                                     ref["h_codes"][r], ref["h_scales"][r],
+                                     g["h"][r, :inp.I], g["hs"][r, :inp.I // 128].astype(np.float64))
+    return allow[rows_used]
+
+
+def close_rows(gy, ry, tol, allow):
+    """Per-row relative L2 <= tol after the allowance, plus the elementwise guard."""
+    gy = np.asarray(gy, np.float64)
+    ry = np.asarray(ry, np.float64)
+    if ry.size == 0:
+        return True
+    num = np.linalg.norm(gy - ry, axis=1)
+    den = np.linalg.norm(ry, axis=1)
+    excess = np.maximum(num - allow, 0.0)
+    row = np.where(den > 0, excess / np.where(den > 0, den, 1.0), excess)
+    e = elem_err(gy, ry)
+    frac = float(np.mean(e > tol))
+    print(f"  window rows: relL2 after allowance max {row.max():.3e} (allowance max "
+          f"{np.max(allow / np.maximum(den, 1e-30)):.3e}) | elementwise max {e.max():.3e}, "
+          f"frac>tol {frac:.2e}", flush=True)
     return row.max() <= tol and e.max() <= 5 * tol and frac <= 1e-3
 
 
@@ -165,7 +257,8 @@ def test_stages_match_oracle(name, over, packed):
         assert rel_err(g["y"][:R][used], ref["y_win"][used]) <= tol
         assert rel_err(out_np(inp, d.out), ref["out"]) <= tol
     else:
-        assert close(g["y"][:R][used], ref["y_win"][used], tol)
+        allow = window_allowance(inp, ref, g, used)
+        assert close_rows(g["y"][:R][used], ref["y_win"][used], tol, allow)
         if inp.shared_I:
             assert close(g["y"][R:R + T], ref["y_shared"], tol)
         assert close(out_np(inp, d.out), ref["out"], tol)
@@ -263,6 +356,35 @@ def test_gemm_schedules_give_identical_output(name, over):
         moe.run(d)
         torch.cuda.synchronize()
         assert torch.equal(ref, d.out), (opt, val)
+    assert moe.device_error() == 0
+
+
+@pytest.mark.parametrize("name,over,packed", [
+    ("prefill4096_zipf_fp8", dict(S=4, T_s=96, H=512, I=256, E=8, k=4, seed=61), False),
+    ("prefill4096_zipf_fp8", dict(S=4, T_s=96, H=512, I=256, E=8, k=4, seed=61), True),
+    ("prefill4096_zipf_fp8", dict(S=3, T_s=80, H=384, I=384, E=5, k=3, seed=62), True),
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=63), True),
+])
+def test_tiled_gemm_matches_oracle_and_streaming_kernel(name, over, packed):
+    """The LDS-tiled kernels (large experts) against the oracle, and bit for bit against
+    the weight-streaming kernels (same MFMAs per output element, same K order)."""
+    inp = synth.make_inputs(name, **over)
+    moe = binding.Moe.for_inputs(inp)
+    moe.set_option(binding.MOE_OPT_TILED_GEMM, 1)
+    moe, d = run(inp, moe=moe, packed=packed)
+    tiled = d.out.clone()
+    ref = layer.moe_layer(inp)
+    assert close(out_np(inp, d.out), ref["out"], TOL["bf16"])
+    g = gpu_state(moe, inp)
+    used = ref["row_src"] >= 0
+    R = inp.S * inp.T_s * inp.k
+    allow = window_allowance(inp, ref, g, used)
+    assert close_rows(g["y"][:R][used], ref["y_win"][used], TOL["bf16"], allow)
+    moe.set_option(binding.MOE_OPT_TILED_GEMM, 2)
+    d.out.zero_()
+    moe.run(d)
+    torch.cuda.synchronize()
+    assert torch.equal(tiled, d.out)
     assert moe.device_error() == 0
 
 
