@@ -46,6 +46,10 @@ def parse():
                     help="experts the CPU oracle evaluates in each timed sample")
     ap.add_argument("--cpu-repeats", type=int, default=3,
                     help="timed CPU oracle samples (the median is reported)")
+    ap.add_argument("--sched", choices=["fence", "sentinel"], default="fence",
+                    help="synchronisation between dispatch and GEMM1")
+    ap.add_argument("--dispatch-cus", type=int, default=0,
+                    help="SENTINEL: CUs of the dispatch stream (multiple of 8; 0 = library default)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -155,7 +159,8 @@ def main():
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(args.workload)
     d = binding.DeviceInputs(inp)
-    moe = binding.Moe.for_inputs(inp)
+    sched = binding.MOE_SCHED_SENTINEL if args.sched == "sentinel" else binding.MOE_SCHED_FENCE
+    moe = binding.Moe.for_inputs(inp, sched=sched, dispatch_cus=args.dispatch_cus)
     if not args.row_major:
         # one-time weight preparation (as at model load), outside the timed region
         moe.pack(d)
@@ -165,13 +170,24 @@ def main():
         moe.run(d)
     torch.cuda.synchronize()
     cnt = moe.routing(inp.S, inp.T_s, inp.k, inp.E)[0].cpu().numpy()
-    moe.set_timing(args.steps)
+    # timed region 1: the layer alone (no timing events: each is a barrier packet
+    # in the queue and would add its own gap to the step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         moe.run(d)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # timed region 2: the same steps with HIP events at every stage boundary, on the
+    # stream each kernel is launched on (stage times and the GEMM1 launch duration)
+    print("[bench] stage timing", file=sys.stderr, flush=True)
+    moe.set_timing(args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.run(d)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     stage_ms, ncalls = moe.read_timing()
     assert ncalls == args.steps
     if moe.device_error():
@@ -204,7 +220,7 @@ def main():
         "config": {"workload": args.workload, "sources": inp.S, "tokens_per_source": inp.T_s,
                    "tokens": inp.S * inp.T_s, "hidden": inp.H, "inter": inp.I, "experts": inp.E,
                    "topk": inp.k, "weights": inp.weight, "shared_inter": inp.shared_I,
-                   "routing": inp.extra.get("routing"), "schedule": "fence",
+                   "routing": inp.extra.get("routing"), "schedule": args.sched,
                    "weight_layout": "row-major" if args.row_major else "packed"},
         "stages_us": {"dispatch": round(avg[0] * 1e3, 2), "gemm1": round(avg[1] * 1e3, 2),
                       "gemm2": round(avg[2] * 1e3, 2), "combine": round(avg[3] * 1e3, 2),
@@ -213,6 +229,7 @@ def main():
         "combine_GBps": round(gbps(nbytes["combine"], avg[3]), 1),
         "gemm_TFLOPs": round(flops / ((avg[1] + avg[2]) * 1e-3) / 1e12, 2),
         "layer_hbm_frac": round(gbps(nbytes["layer"], ms_step) / HBM_PEAK_GBPS, 4),
+        "us_per_step_with_stage_events": round((t3 - t2) * 1e6 / args.steps, 2),
         "algorithmic_bytes": nbytes,
         "roofline": {"kernel": "gemm1 (FP8 grouped GEMM + SwiGLU + requant)", "bound": "hbm",
                      "achieved": round(g1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

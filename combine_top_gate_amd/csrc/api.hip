@@ -30,7 +30,9 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 
 constexpr int kStages = 5;  // dispatch, gemm1, gemm2, combine, layer
 constexpr int kSchedWords = 16 + MOE_MAX_EXPERTS + 1 + 15;
-constexpr uint32_t kSpinLimit = 1u << 22;  // ~0.2 s of s_sleep polling
+constexpr uint32_t kSpinLimit = 1u << 22;  // persistent GEMM: ~0.2 s of s_sleep polling
+constexpr uint32_t kSentinelSpin = 1u << 20;  // SENTINEL GEMM1: polls before a wait gives up
+constexpr int kXcds = 8;                     // CU mask bits are spread over the XCDs
 constexpr double kTiledRows = 192.0;       // mean rows per expert from which the tiled GEMM runs
 
 }  // namespace
@@ -54,7 +56,16 @@ struct moe_ctx {
   uint32_t* err = nullptr;
   uint32_t* sched = nullptr;  // persistent GEMM: queue heads, exit count, per-group counters
   int* plan = nullptr;        // tiled GEMM: tile table and work counters
+  uint32_t* sync = nullptr;   // SENTINEL: rflag[MOE_MAX_SRC], dflag[..], arrive[..]
   int n_cu = 0;
+  // SENTINEL with dispatch_cus > 0: dispatch and GEMM1 streams on disjoint CU sets and
+  // their fork/join events; with 0, the dispatch runs inside the GEMM1 launch
+  hipStream_t s_disp = nullptr, s_comp = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_disp = nullptr, ev_g1 = nullptr;
+  int dispatch_cus = 0;
+  uint32_t epoch = 0;
+  uint32_t spin_limit = kSentinelSpin;
+  int opt_stall = 0;
   // options
   int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0;
   // state of the last dispatch
@@ -69,10 +80,10 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-BatchDims dims(const moe_ctx* c) {
+BatchDims dims(const moe_ctx* c, int T_s) {
   BatchDims d;
   d.S = c->cfg.n_src;
-  d.T_s = c->T_s;
+  d.T_s = T_s;
   d.k = c->cfg.topk;
   d.E = c->cfg.n_experts;
   d.H = c->cfg.hidden;
@@ -83,6 +94,8 @@ BatchDims dims(const moe_ctx* c) {
   d.hstride = c->hstride;
   return d;
 }
+
+BatchDims dims(const moe_ctx* c) { return dims(c, c->T_s); }
 
 moe_status check_config(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
@@ -109,6 +122,9 @@ moe_status check_config(const moe_config* c) {
                 c->act, c->weight, c->out);
   if (c->sched != MOE_SCHED_FENCE && c->sched != MOE_SCHED_SENTINEL)
     return fail(MOE_ERR_INVALID_ARG, "unknown schedule %d", c->sched);
+  if (c->dispatch_cus < 0 || c->dispatch_cus % kXcds)
+    return fail(MOE_ERR_INVALID_ARG, "dispatch_cus %d is not 0 or a positive multiple of %d", c->dispatch_cus,
+                kXcds);
   const int64_t R = (int64_t)c->n_src * c->max_tokens * c->topk;
   if (R > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "window of %lld rows is too large", (long long)R);
   return MOE_OK;
@@ -151,8 +167,6 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   *out = nullptr;
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->sched == MOE_SCHED_SENTINEL)
-    return fail(MOE_ERR_UNSUPPORTED, "the SENTINEL schedule is not available in this build");
   moe_ctx* c = new moe_ctx();
   c->cfg = *cfg;
   auto cleanup = [&](moe_status s) {
@@ -182,16 +196,34 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (e = alloc((void**)&c->row_src, (size_t)c->R_cap * 4)) != hipSuccess ||
       (e = alloc((void**)&c->err, 4)) != hipSuccess ||
       (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess ||
-      (e = alloc((void**)&c->plan, (size_t)tiled_plan_words() * 4)) != hipSuccess)
+      (e = alloc((void**)&c->plan, (size_t)tiled_plan_words() * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->sync, 3 * MOE_MAX_SRC * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "workspace allocation failed: %s", hipGetErrorString(e)));
   if ((e = hipMemset(c->err, 0, 4)) != hipSuccess || (e = hipMemset(c->cnt, 0, (size_t)S * E * 4)) != hipSuccess ||
       (e = hipMemset(c->sched, 0, kSchedWords * 4)) != hipSuccess ||
-      (e = hipMemset(c->off, 0, (size_t)S * E * 4)) != hipSuccess)
+      (e = hipMemset(c->off, 0, (size_t)S * E * 4)) != hipSuccess ||
+      (e = hipMemset(c->sync, 0, 3 * MOE_MAX_SRC * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)));
   hipDeviceProp_t prop;
   if ((e = hipGetDeviceProperties(&prop, c->device)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e)));
   c->n_cu = prop.multiProcessorCount;
+  if (cfg->sched == MOE_SCHED_SENTINEL && cfg->dispatch_cus > 0) {
+    // two streams on disjoint CU sets: dispatch gets dispatch_cus CUs, GEMM1 the rest
+    const int dcu = cfg->dispatch_cus;
+    if (dcu >= c->n_cu)
+      return cleanup(fail(MOE_ERR_INVALID_ARG, "dispatch_cus %d leaves no CU of %d for the GEMM", dcu, c->n_cu));
+    c->dispatch_cus = dcu;
+    std::vector<uint32_t> dm((c->n_cu + 31) / 32, 0u), cm(dm.size(), 0u);
+    for (int i = 0; i < c->n_cu; ++i) (i < dcu ? dm : cm)[i >> 5] |= 1u << (i & 31);
+    if ((e = hipExtStreamCreateWithCUMask(&c->s_disp, (uint32_t)dm.size(), dm.data())) != hipSuccess ||
+        (e = hipExtStreamCreateWithCUMask(&c->s_comp, (uint32_t)cm.size(), cm.data())) != hipSuccess)
+      return cleanup(fail(MOE_ERR_UNSUPPORTED, "CU-masked streams for SENTINEL: %s", hipGetErrorString(e)));
+    if ((e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_disp, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_g1, hipEventDisableTiming)) != hipSuccess)
+      return cleanup(fail(MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e)));
+  }
   *out = c;
   return MOE_OK;
 }
@@ -200,16 +232,25 @@ moe_status moe_destroy(moe_ctx* c) {
   if (!c) return MOE_OK;
   (void)hipDeviceSynchronize();
   for (auto ev : c->ev) (void)hipEventDestroy(ev);
-  void* bufs[] = {c->win, c->wsc, c->h, c->hs, c->y,     c->cnt,   c->off,
-                  c->dst_row, c->row_src, c->err, c->sched, c->plan};
+  for (hipEvent_t ev : {c->ev_fork, c->ev_disp, c->ev_g1})
+    if (ev) (void)hipEventDestroy(ev);
+  for (hipStream_t st : {c->s_disp, c->s_comp})
+    if (st) (void)hipStreamDestroy(st);
+  void* bufs[] = {c->win,     c->wsc,     c->h,   c->hs,    c->y,    c->cnt,
+                  c->off,     c->dst_row, c->row_src, c->err, c->sched, c->plan, c->sync};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete c;
   return MOE_OK;
 }
 
-moe_status moe_dispatch(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
-                        const int32_t* ids, hipStream_t stream) {
+}  // extern "C"
+
+// Validates the dispatch arguments and fills `da` (nothing is launched; T_s == 0 leaves
+// da.T_s = 0).  publish: SENTINEL flags for this call's epoch; blocks: workgroups
+// the chunks should spread over.
+static moe_status dispatch_prepare(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                                   const int32_t* ids, bool publish, int blocks, DispatchArgs& da) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
   const moe_config& cf = c->cfg;
   if (T_s < 0 || T_s > cf.max_tokens)
@@ -232,16 +273,69 @@ moe_status moe_dispatch(moe_ctx* c, int32_t T_s, const void* const* x, const flo
   }
   c->T_s = T_s;
   c->src = src;
+  da = DispatchArgs{};
   if (T_s == 0) return MOE_OK;
-  RouteArgs ra{ids, c->cnt, c->off, c->dst_row, c->row_src, c->err, cf.n_src, T_s, cf.topk, cf.n_experts};
-  HIP_TRY(launch_route(ra, stream));
-  ScatterArgs sa{src, c->dst_row, c->win, fp8 ? c->wsc : nullptr, cf.n_src, T_s, cf.topk, c->row_bytes,
-                 fp8 ? cf.hidden / 128 : 0};
-  HIP_TRY(launch_scatter(sa, stream));
+  da.ids = ids;
+  da.cnt = c->cnt;
+  da.off = c->off;
+  da.dst_row = c->dst_row;
+  da.row_src = c->row_src;
+  da.err = c->err;
+  da.src = src;
+  da.win = c->win;
+  da.wsc = fp8 ? c->wsc : nullptr;
+  da.S = cf.n_src;
+  da.T_s = T_s;
+  da.k = cf.topk;
+  da.E = cf.n_experts;
+  da.row_bytes = c->row_bytes;
+  da.nsc = fp8 ? cf.hidden / 128 : 0;
+  da.tpb = dispatch_tokens_per_block(T_s, cf.topk, blocks, cf.n_src);
+  if (publish) {
+    da.rflag = c->sync;
+    da.dflag = c->sync + MOE_MAX_SRC;
+    da.arrive = c->sync + 2 * MOE_MAX_SRC;
+    da.epoch = c->epoch;
+  }
   return MOE_OK;
 }
 
-static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed) {
+// Validates and launches the dispatch kernel (about four workgroups per CU it may use).
+static moe_status dispatch_impl(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                                const int32_t* ids, hipStream_t stream, bool publish) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  DispatchArgs da;
+  moe_status st = dispatch_prepare(c, T_s, x, x_scale, ids, publish, 4 * (publish ? c->dispatch_cus : c->n_cu), da);
+  if (st != MOE_OK || da.T_s == 0) return st;
+  HIP_TRY(launch_dispatch(da, stream));
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_dispatch(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                        const int32_t* ids, hipStream_t stream) {
+  return dispatch_impl(c, T_s, x, x_scale, ids, stream, false);
+}
+
+static bool use_tiled(const moe_ctx* c, const BatchDims& d) {
+  const moe_config& cf = c->cfg;
+  if (cf.act == MOE_F32 || cf.weight == MOE_FP4_E2M1) return false;
+  return c->opt_tiled == 1 || (c->opt_tiled == 0 && (double)d.R / d.E >= kTiledRows);
+}
+
+// SENTINEL overlaps dispatch with the decode GEMM1 (weight-streaming kernels, two
+// launches); the tiled prefill, fp32 and persistent paths run in stream order.
+static bool sentinel_applies(const moe_ctx* c, int T_s) {
+  if (c->cfg.sched != MOE_SCHED_SENTINEL || c->cfg.act == MOE_F32 || c->opt_persistent || T_s <= 0) return false;
+  return !use_tiled(c, dims(c, T_s));
+}
+
+// sn: SENTINEL -- GEMM1 polls the dispatch's flags.  fused != null: the dispatch chunks
+// run in the GEMM1 launch itself, on `stream`; otherwise GEMM1 runs on the compute
+// stream and GEMM2 joins both streams back into `stream`.
+static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed, bool sn = false,
+                             const DispatchArgs* fused = nullptr) {
   const moe_config& cf = c->cfg;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
@@ -295,9 +389,23 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
   GemmArgs g1 = g;
   // many rows per expert: the LDS-tiled, MFMA-bound kernels (FP8 weights)
-  const double rows_per_expert = (double)d.R / d.E;
-  const bool tiled = !f32 && !fp4 && (c->opt_tiled == 1 || (c->opt_tiled == 0 && rows_per_expert >= kTiledRows));
-  if (!tiled && (f32 || !c->opt_persistent)) {
+  const bool tiled = use_tiled(c, d);
+  if (sn) {
+    g1.rflag = c->sync;
+    g1.dflag = c->sync + MOE_MAX_SRC;
+    g1.epoch = c->opt_stall ? c->epoch ^ 0x80000000u : c->epoch;  // stall: an epoch never published
+    g1.spin_limit = c->spin_limit;
+    if (fused) {
+      HIP_TRY(launch_gemm1_lowp(g1, cf.weight, packed, nt, stream, fused));
+      if (timed) record(c, 2, stream);
+    } else {
+      HIP_TRY(launch_gemm1_lowp(g1, cf.weight, packed, nt, c->s_comp));
+      if (timed) record(c, 2, c->s_comp);
+      HIP_TRY(hipEventRecord(c->ev_g1, c->s_comp));
+      HIP_TRY(hipStreamWaitEvent(stream, c->ev_disp, 0));
+      HIP_TRY(hipStreamWaitEvent(stream, c->ev_g1, 0));
+    }
+  } else if (!tiled && (f32 || !c->opt_persistent)) {
     HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
     if (timed) record(c, 2, stream);
   }
@@ -332,7 +440,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     if (timed) record(c, 2, stream);
     return MOE_OK;
   }
-  if (f32 || !c->opt_persistent) {
+  if (f32 || !c->opt_persistent || sn) {
     HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
     return MOE_OK;
   }
@@ -383,10 +491,32 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
   if (T_s > 0 && (!topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
   const bool timed = c->timing_n < c->timing_cap;
   if (timed) record(c, 0, stream);
-  moe_status st = moe_dispatch(c, T_s, x, x_scale, ids, stream);
-  if (st != MOE_OK) return st;
-  if (timed) record(c, 1, stream);
-  st = gemm_stage(c, w, stream, timed);
+  const bool sn = sentinel_applies(c, T_s);
+  moe_status st;
+  DispatchArgs fused;
+  const bool use_fused = sn && c->dispatch_cus == 0;
+  if (use_fused) {
+    // the dispatch chunks become the first workgroups of the GEMM1 launch
+    c->epoch = c->epoch + 1 ? c->epoch + 1 : 1;  // 0 (the flags' initial value) is never an epoch
+    st = dispatch_prepare(c, T_s, x, x_scale, ids, true, 2 * c->n_cu, fused);
+    if (st != MOE_OK) return st;
+    if (timed) record(c, 1, stream);
+  } else if (sn) {
+    // fork: dispatch and GEMM1 start together on their CU sets once `stream` is here
+    HIP_TRY(hipEventRecord(c->ev_fork, stream));
+    HIP_TRY(hipStreamWaitEvent(c->s_disp, c->ev_fork, 0));
+    HIP_TRY(hipStreamWaitEvent(c->s_comp, c->ev_fork, 0));
+    c->epoch = c->epoch + 1 ? c->epoch + 1 : 1;  // 0 (the flags' initial value) is never an epoch
+    st = dispatch_impl(c, T_s, x, x_scale, ids, c->s_disp, true);
+    if (st != MOE_OK) return st;
+    if (timed) record(c, 1, c->s_disp);
+    HIP_TRY(hipEventRecord(c->ev_disp, c->s_disp));
+  } else {
+    st = dispatch_impl(c, T_s, x, x_scale, ids, stream, false);
+    if (st != MOE_OK) return st;
+    if (timed) record(c, 1, stream);
+  }
+  st = gemm_stage(c, w, stream, timed, sn, use_fused ? &fused : nullptr);
   if (st != MOE_OK) return st;
   if (timed) record(c, 3, stream);
   st = moe_combine(c, topk_w, out, stream);
@@ -530,6 +660,14 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
     case MOE_OPT_TILED_GEMM:
       if (v < 0 || v > 2) break;
       c->opt_tiled = v;
+      return MOE_OK;
+    case MOE_OPT_SENTINEL_SPIN:
+      if (v < 0) break;
+      c->spin_limit = v ? (uint32_t)v : kSentinelSpin;
+      return MOE_OK;
+    case MOE_OPT_SENTINEL_STALL:
+      if (v != 0 && v != 1) break;
+      c->opt_stall = v;
       return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);

@@ -31,6 +31,7 @@
 // k = 64+16g..64+16g+15 in bytes 16..31; an FP4 operand holds k = 32g..32g+31 as
 // nibbles (element 2i in the low nibble of byte i) and lane l's e8m0 scale covers
 // exactly those 32 k.  The result's lane l, register i is row 4g+i, column l%16.
+#include "dispatch_chunk.h"
 #include "kernels.h"
 #include "pack_layout.h"
 
@@ -223,9 +224,9 @@ __device__ __forceinline__ void stage_token_scales(float* s_tsc, const float* co
 }
 
 // Flat work list: routed expert g has nb_r entries, then the shared expert nb_s.
-__device__ __forceinline__ void work_item(const BatchDims& d, int nb_r, int nb_s, int& g, int& nb) {
+__device__ __forceinline__ void work_item(const BatchDims& d, int nb_r, int nb_s, int b, int& g, int& nb) {
   const int total = d.E * nb_r + nb_s;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = xcd_remap(b, total);
   if (L < d.E * nb_r) {
     g = L / nb_r;
     nb = L - g * nb_r;
@@ -270,6 +271,38 @@ __device__ __forceinline__ int seg_row(const SegTable& t, int S, int m) {
   int s = 0;
   while (s + 1 < S && m >= t.pre[s + 1]) ++s;
   return t.row0[s] + (m - t.pre[s]);
+}
+
+// SENTINEL handshake of the routed experts' GEMM1 ("GC-MoE", token-ring handshake:
+// the GEMM polls what dispatch publishes instead of waiting for its kernel to end).
+// Lanes s < S of wave 0 poll flag[s] with relaxed loads and sleeps until it holds the
+// epoch -- every source when t is null, else only the sources with rows for this
+// group -- and then take one agent-scope acquire fence; the barrier orders the other
+// waves after it.  A wait that exceeds spin_limit polls gives up: the work item is
+// skipped and MOE_DEVERR_TIMEOUT latched.  Uniform over the workgroup.
+__device__ __forceinline__ bool sentinel_wait(const GemmArgs& p, const uint32_t* flag, const SegTable* t) {
+  __shared__ int s_fail;
+  if (threadIdx.x == 0) s_fail = 0;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const bool need = s < p.d.S && (t == nullptr || t->pre[s + 1] > t->pre[s]);
+    if (need) {
+      uint32_t it = 0;
+      while (__hip_atomic_load(flag + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+        if (++it > p.spin_limit) {
+          s_fail = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  const bool ok = s_fail == 0;
+  if (!ok && threadIdx.x == 0) atomicOr(p.err, MOE_DEVERR_TIMEOUT);
+  return ok;
 }
 
 // Token rows of one pass for this lane: column r16 of each 16-token tile.  Rows past
@@ -374,6 +407,9 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
   int nb = nb_item;
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
+  // the shared expert reads the source buffers, so only routed groups wait
+  const bool sentinel = p.rflag != nullptr && !shared;
+  if (sentinel && !sentinel_wait(p, p.rflag, nullptr)) return;
   const int M = load_segments(p, g, seg);
   // the shared expert's rows are split into chunks, each its own work item
   int mb = 0, me = M;
@@ -411,6 +447,8 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = mt >> 1;
   }
+  // the weight scales are in flight while this group's window rows are awaited
+  if (sentinel && !sentinel_wait(p, p.dflag, &seg)) return;
 
   for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
@@ -425,13 +463,23 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
   }
 }
 
+// ndisp > 0 (fused SENTINEL launch): workgroups 0 .. ndisp-1 run the dispatch chunks
+// (da, `chunks` per source; a multiple of 8 so every XCD keeps its b % 8 blocks) and
+// the work items follow.  A GPU places a launch's workgroups in index order, so every
+// dispatch chunk is resident before any work item that waits for it.
 template <int NTMAX, int WFMT, bool PACKED>
-__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p) {
+__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs da, int ndisp, int chunks) {
   __shared__ float s_amax[4][kMaxTok];
   __shared__ float s_tsc[kMaxKB * kMaxTok];
   __shared__ SegTable seg;
+  static_assert(sizeof(DispatchSmem) <= sizeof(s_tsc), "the dispatch chunk borrows s_tsc");
+  if ((int)blockIdx.x < ndisp) {
+    const int b = blockIdx.x;
+    if (b < da.S * chunks) dispatch_chunk(da, b / chunks, b % chunks, chunks, *reinterpret_cast<DispatchSmem*>(s_tsc));
+    return;
+  }
   int g, nb;
-  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, g, nb);
+  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, (int)blockIdx.x - ndisp, g, nb);
   gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, seg);
 }
 
@@ -532,7 +580,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   __shared__ SegTable seg;
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
-  work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, g, nb);
+  work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, blockIdx.x, g, nb);
   gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, seg);
 }
 
@@ -620,16 +668,23 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
 }
 
 template <int WFMT, bool PACKED>
-hipError_t launch1(const GemmArgs& a, int nt, hipStream_t st) {
-  const dim3 grid(a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
+hipError_t launch1(const GemmArgs& a, int nt, const DispatchArgs* fused, hipStream_t st) {
+  DispatchArgs da{};
+  int ndisp = 0, chunks = 0;
+  if (fused) {
+    da = *fused;
+    chunks = dispatch_chunks(da);
+    ndisp = (da.S * chunks + 7) / 8 * 8;
+  }
+  const dim3 grid(ndisp + a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
   if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
   else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
   else if (nt == 4 || WFMT != MOE_FP4_E2M1)
-    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
   else
-    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
   return hipGetLastError();
 }
 
@@ -691,10 +746,13 @@ int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles) {
                 : experts_blocks_per_cu<MOE_FP8_E4M3, false>(tok_tiles);
 }
 
-hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {
+hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st,
+                             const DispatchArgs* fused) {
   if (weight_fmt == MOE_FP4_E2M1)
-    return packed ? launch1<MOE_FP4_E2M1, true>(a, tok_tiles, st) : launch1<MOE_FP4_E2M1, false>(a, tok_tiles, st);
-  return packed ? launch1<MOE_FP8_E4M3, true>(a, tok_tiles, st) : launch1<MOE_FP8_E4M3, false>(a, tok_tiles, st);
+    return packed ? launch1<MOE_FP4_E2M1, true>(a, tok_tiles, fused, st)
+                  : launch1<MOE_FP4_E2M1, false>(a, tok_tiles, fused, st);
+  return packed ? launch1<MOE_FP8_E4M3, true>(a, tok_tiles, fused, st)
+                : launch1<MOE_FP8_E4M3, false>(a, tok_tiles, fused, st);
 }
 
 hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {

@@ -6,27 +6,31 @@
 #include "common.h"
 
 // ---- dispatch ---------------------------------------------------------------
-struct RouteArgs {
+// One launch: route (counts, offsets, row maps) and scatter of the token rows.
+constexpr int kMaxDispatchPairs = 1024;  // (token, slot) pairs per dispatch workgroup
+struct DispatchArgs {
   const int32_t* ids;  // [S][T_s][k]
   int32_t* cnt;        // [S][E]
   int32_t* off;        // [S][E]
   int32_t* dst_row;    // [S][T_s][k]
   int32_t* row_src;    // [S*T_s*k]
   uint32_t* err;
-  int S, T_s, k, E;
-};
-hipError_t launch_route(const RouteArgs& a, hipStream_t st);
-
-struct ScatterArgs {
   SrcPtrs src;
-  const int32_t* dst_row;  // [S][T_s][k]
-  uint8_t* win;            // [R][row_bytes]
-  float* wsc;              // [R][nsc] or null
-  int S, T_s, k;
-  int row_bytes;           // bytes per token row (multiple of 16)
-  int nsc;                 // scales per row (0 = none)
+  uint8_t* win;        // [R][row_bytes]
+  float* wsc;          // [R][nsc] or null
+  int S, T_s, k, E;
+  int row_bytes;       // bytes per token row (multiple of 16)
+  int nsc;             // scales per row (0 = none)
+  int tpb;             // tokens per workgroup (tpb * k <= kMaxDispatchPairs)
+  // SENTINEL publication (all null under FENCE): per-source epoch flags
+  uint32_t* rflag;     // [S] counts and offsets written
+  uint32_t* dflag;     // [S] every window row of the source written
+  uint32_t* arrive;    // [S] arrival counters (zero between calls)
+  uint32_t epoch;
 };
-hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
+int dispatch_tokens_per_block(int T_s, int k, int blocks_wanted, int S);
+int dispatch_chunks(const DispatchArgs& a);  // workgroups per source
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
 // ---- grouped GEMMs ----------------------------------------------------------
 // One launch covers every routed expert and, when present, the shared expert
@@ -54,10 +58,17 @@ struct GemmArgs {
   uint32_t* err;
   int sh_chunks;      // the shared expert's rows are split into this many work items
   int sh_chunk_rows;  // rows per chunk (multiple of 16)
+  // SENTINEL (GEMM1 of the routed experts): wait for rflag/dflag[s] == epoch; null = FENCE
+  const uint32_t* rflag;
+  const uint32_t* dflag;
+  uint32_t epoch;
+  uint32_t spin_limit;
 };
 // weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; packed: weights in the pack_layout.h order;
 // tok_tiles: most 16-token tiles per pass (2..4)
-hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
+// fused: also run these dispatch chunks in the launch's first workgroups (SENTINEL)
+hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st,
+                             const DispatchArgs* fused = nullptr);
 hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st);
 // Both low-precision GEMMs in one persistent launch (work queues, see gemm_lowp.hip).
 struct ExpertsArgs {

@@ -33,14 +33,26 @@
  *
  * Synchronisation between dispatch and GEMM follows one of two schedules
  * ["One-Sided ... over NVLink", abstract: Fence for throughput, Sentinel for
- * latency].  FENCE: the steps run in stream order.  SENTINEL: dispatch runs on
- * a stream restricted to a few CUs while the GEMM kernel is already resident on
- * the others; each source publishes an epoch tag once its rows and counts are in
- * place and the GEMM polls those tags before it reads a window (the device-side
- * counter handshake of "GC-MoE", full text, and of "GC-MoE: Decoupling MoE
- * Communication and Computation with CUDA Green Contexts", section "Three-Node
- * CUDA Graph and token-ring Handshake").  Epoch tags grow monotonically, so no
- * clean pass is needed between calls.
+ * latency].  FENCE: the steps run in stream order.  SENTINEL (moe_layer): dispatch
+ * and GEMM1 run at the same time.  Each source publishes an epoch tag once its
+ * counts and offsets are written and another once all of its window rows are; a
+ * GEMM1 workgroup polls the first kind for every source, builds its expert's row
+ * table, issues its weight-scale loads, and then waits only for the sources that
+ * hold rows of its expert (the device-side counter handshake of "GC-MoE", full
+ * text, and of "GC-MoE: Decoupling MoE Communication and Computation with CUDA
+ * Green Contexts", section "Three-Node CUDA Graph and token-ring Handshake").
+ * Epoch tags grow monotonically, so no clean pass is needed between calls.
+ * Two forms, chosen by dispatch_cus:
+ *   0   the dispatch chunks are the first workgroups of the GEMM1 launch itself
+ *       (one queue; workgroups are placed in index order, so a waiting GEMM
+ *       workgroup never holds back the chunk it waits for);
+ *   >0  the dispatch kernel runs on a stream restricted to dispatch_cus CUs and
+ *       GEMM1 on a stream holding the other CUs (the partition of the "GC-MoE"
+ *       pages); GEMM2 and the combine run on the caller's stream after both
+ *       streams join.  Each fork and join is a wait between hardware queues.
+ * SENTINEL applies to the FP8/MXFP4 decode kernels; the tiled prefill GEMM, the
+ * fp32 path, the persistent GEMM and the separate stage calls run in stream
+ * order (FENCE).
  *
  * Conventions
  *   - Every data pointer is a DEVICE pointer owned by the caller, except the
@@ -104,7 +116,9 @@ typedef struct moe_config {
   moe_dtype weight;       /* MOE_FP8_E4M3 or MOE_FP4_E2M1 (with MOE_FP8_E4M3 act), or MOE_F32 */
   moe_dtype out;          /* MOE_BF16 (FP8 act) or MOE_F32 (F32 act) */
   moe_schedule sched;     /* FENCE or SENTINEL */
-  int32_t dispatch_cus;   /* SENTINEL: CUs given to dispatch (0 = default) */
+  int32_t dispatch_cus;   /* SENTINEL: 0 = dispatch inside the GEMM1 launch; else the
+                             CUs of a separate dispatch stream, a multiple of 8 (the
+                             mask spreads over the 8 XCDs) below the GPU's CU count */
 } moe_config;
 
 /*
@@ -219,13 +233,20 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *   MOE_OPT_TILED_GEMM       0: automatic (LDS-tiled MFMA kernels from 192 mean rows per
  *                            expert, FP8 weights); 1: always tiled (FP8 weights);
  *                            2: never (the weight-streaming kernels).
+ *   MOE_OPT_SENTINEL_SPIN    SENTINEL: polls of one flag before a GEMM1 workgroup gives
+ *                            up (latching MOE_DEVERR_TIMEOUT); 0: default (2^20).
+ *   MOE_OPT_SENTINEL_STALL   1: GEMM1 waits for an epoch the dispatch never publishes,
+ *                            so every routed wait times out -- a test of the failure
+ *                            path (the layer output is then invalid); 0: off.
  * Unknown options or values return MOE_ERR_INVALID_ARG.
  */
 typedef enum {
   MOE_OPT_PERSISTENT_GEMM = 0,
   MOE_OPT_TOKEN_TILES = 1,
   MOE_OPT_QUEUE = 2,
-  MOE_OPT_TILED_GEMM = 3
+  MOE_OPT_TILED_GEMM = 3,
+  MOE_OPT_SENTINEL_SPIN = 4,
+  MOE_OPT_SENTINEL_STALL = 5
 } moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 
@@ -238,7 +259,11 @@ moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
  * them and returns, for the calls recorded since the last read, the summed
  * milliseconds of [0] dispatch, [1] GEMM1 (+SwiGLU+requant), [2] GEMM2, [3] combine,
  * [4] whole layer, and the number of calls in *n_calls.  With the persistent GEMM
- * kernel, [1] holds both GEMMs and [2] is 0.
+ * kernel or the tiled GEMM, [1] holds both GEMMs and [2] is 0.  Under SENTINEL,
+ * [0] is the dispatch on its own stream, [1] runs from the end of the dispatch to
+ * the end of GEMM1 (the part of GEMM1 not hidden behind it) and [2] includes the
+ * join of the two streams; in the fused form [0] is 0 and [1] holds the launch
+ * that runs both.
  */
 moe_status moe_set_timing(moe_ctx* ctx, int32_t max_calls);
 moe_status moe_read_timing(moe_ctx* ctx, float* ms_sum5, int32_t* n_calls);

@@ -44,7 +44,7 @@ def _create(lib, cfg):
     ("n_src", 33, "n_src"), ("topk", 0, "topk"), ("n_experts", 300, "n_experts"),
     ("shared_inter", 64, "shared_inter"), ("max_tokens", -1, "max_tokens"),
     ("out", binding.MOE_F32, "dtype"), ("weight", binding.MOE_F32, "dtype"),
-    ("sched", 7, "schedule"),
+    ("sched", 7, "schedule"), ("dispatch_cus", 12, "dispatch_cus"), ("dispatch_cus", -8, "dispatch_cus"),
 ])
 def test_invalid_configs_rejected_on_host(lib, field, value, needle):
     cfg = binding.make_config(8, 16, 7168, 2048, 32, 8)

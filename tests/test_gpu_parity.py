@@ -402,11 +402,91 @@ def test_many_back_to_back_calls_reuse_scheduler_state():
     assert moe.device_error() == 0
 
 
+SENTINEL_CASES = [
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=71), 0),
+    ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=72), 0),
+    ("decode128_fp8", dict(S=8, T_s=5, H=256, I=128, E=16, k=4, seed=73), 8),
+    ("decode128_fp8", dict(S=4, T_s=3, H=256, I=256, E=6, k=2, seed=74), 32),
+]
+
+
+def _fence_and_sentinel(inp, dispatch_cus=0, packed=True):
+    outs = []
+    for sched in (binding.MOE_SCHED_FENCE, binding.MOE_SCHED_SENTINEL):
+        moe = binding.Moe.for_inputs(inp, sched=sched, dispatch_cus=dispatch_cus)
+        moe, d = run(inp, moe=moe, packed=packed)
+        outs.append((moe, d))
+    return outs
+
+
+@pytest.mark.parametrize("name,over,dcu", SENTINEL_CASES)
+def test_sentinel_matches_fence_and_oracle(name, over, dcu):
+    """SENTINEL only changes when GEMM1 may start: the same kernels give the same bits."""
+    inp = synth.make_inputs(name, **over)
+    (mf, df), (ms, ds) = _fence_and_sentinel(inp, dcu)
+    assert ms.device_error() == 0
+    assert torch.equal(df.out, ds.out)
+    ref = layer.moe_layer(inp)
+    check_routing(gpu_state(ms, inp), ref)
+    assert close(out_np(inp, ds.out), ref["out"], TOL[inp.out])
+
+
+@pytest.mark.parametrize("name,dcu", [("decode8_fp8", 0), ("decode128_fp8", 0), ("decode128_fp8", 16)])
+def test_sentinel_full_size(name, dcu):
+    inp = _full(name)
+    (mf, df), (ms, ds) = _fence_and_sentinel(inp, dcu)
+    assert ms.device_error() == 0
+    assert torch.equal(df.out, ds.out)
+    g = gpu_state(ms, inp)
+    ref_route = layer.dispatch(inp.ids, inp.E)
+    for key in ("cnt", "off", "dst_row", "row_src"):
+        assert np.array_equal(g[key], ref_route[key])
+
+
+def test_sentinel_back_to_back_calls():
+    """Epoch tags and arrival counters are reused across calls of varying size."""
+    over = dict(S=4, H=256, I=128, E=8, k=3)
+    fence = binding.Moe(binding.make_config(4, 6, 256, 128, 8, 3))
+    sent = binding.Moe(binding.make_config(4, 6, 256, 128, 8, 3, sched=binding.MOE_SCHED_SENTINEL))
+    for i, T_s in enumerate([6, 1, 4, 6, 2, 5]):
+        inp = synth.make_inputs("decode128_fp8", T_s=T_s, seed=80 + i, **over)
+        print(f"[gpu case] back-to-back call {i} T_s={T_s}", flush=True)
+        d = binding.DeviceInputs(inp)
+        fence.run(d)
+        want = d.out.clone()
+        d.out.zero_()
+        sent.run(d)
+        torch.cuda.synchronize()
+        assert torch.equal(want, d.out), i
+    assert sent.device_error() == 0
+
+
+def test_sentinel_timeout_is_latched_and_recovers():
+    """A wait that never completes gives up after its spin limit (forced from the host),
+    latches MOE_DEVERR_TIMEOUT, and the next call is correct again."""
+    inp = synth.make_inputs("decode128_fp8", S=2, T_s=3, H=256, I=128, E=4, k=2, seed=90)
+    (mf, df), (ms, ds) = _fence_and_sentinel(inp)
+    want = df.out.clone()
+    ms.set_option(binding.MOE_OPT_SENTINEL_SPIN, 64)
+    ms.set_option(binding.MOE_OPT_SENTINEL_STALL, 1)
+    ms.run(ds)
+    torch.cuda.synchronize()
+    assert ms.device_error() & binding.MOE_DEVERR_TIMEOUT
+    ms.set_option(binding.MOE_OPT_SENTINEL_STALL, 0)
+    ms.set_option(binding.MOE_OPT_SENTINEL_SPIN, 0)
+    ds.out.zero_()
+    ms.run(ds)
+    torch.cuda.synchronize()
+    assert ms.device_error() == 0
+    assert torch.equal(want, ds.out)
+
+
 def test_invalid_options():
     inp = synth.make_inputs("decode128_fp8", S=2, T_s=2, H=128, I=128, E=4, k=2)
     moe = binding.Moe.for_inputs(inp)
     for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 7), (binding.MOE_OPT_QUEUE, 3),
-                     (binding.MOE_OPT_PERSISTENT_GEMM, 2), (9, 0)]:
+                     (binding.MOE_OPT_PERSISTENT_GEMM, 2), (binding.MOE_OPT_SENTINEL_SPIN, -1),
+                     (binding.MOE_OPT_SENTINEL_STALL, 2), (9, 0)]:
         with pytest.raises(binding.MoeError):
             moe.set_option(opt, val)
 
