@@ -96,16 +96,15 @@ __device__ __forceinline__ float lane_value(const float (&v)[2], int kb) {
   return __int_as_float(kb < 64 ? lo : hi);
 }
 
-// One K slab of operands for one wave.
-template <int WFMT, int NT>
-struct Slab {
+// One K slab of one wave's weights.
+template <int WFMT>
+struct WSlab {
   u32x4 w[4][WeightFmt<WFMT>::kLoads];
-  uint32_t e;              // FP4: e8m0 of tile mt in byte mt
-  u32x4 t[NT][2];
+  uint32_t e;  // FP4: e8m0 of tile mt in byte mt
 };
 
-template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void load_slab_w(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws, int kb) {
+template <int WFMT, bool PACKED>
+__device__ __forceinline__ void load_wslab(WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws, int kb) {
   constexpr int WL = WeightFmt<WFMT>::kLoads;
   if constexpr (PACKED) {
     const uint8_t* p = ws.base + (int64_t)kb * (4 * WL * 1024);
@@ -131,35 +130,51 @@ __device__ __forceinline__ void load_slab_w(Slab<WFMT, NT>& s, const WSrc<WFMT, 
   }
 }
 
-template <int WFMT, int NT>
-__device__ __forceinline__ void load_slab_t(Slab<WFMT, NT>& s, const uint8_t* const (&trow)[NT], int kb) {
+// A pass's token tiles (16*NT rows) are staged K slab by K slab in LDS, shared by the
+// workgroup's four waves (each wave multiplies the same tokens with its own weight
+// rows).  A staged row takes kTokStride bytes: 128 + 16 of padding, which keeps the
+// B-operand reads (16 rows x 4 lane groups per instruction) free of bank conflicts.
+constexpr int kTokStride = 144;
+
+// This thread's share of staging one K slab: chunk c = threadIdx.x + 256 i is bytes
+// 16 (c % 8) .. +15 of token row c / 8.
+template <int NT>
+struct TokStage {
+  static constexpr int C = (NT * 16 * 8 + 255) / 256;
+  const uint8_t* src[C];  // the chunk at K slab 0, or null (no chunk)
+  int dst[C];             // byte offset in a staging buffer
+};
+
+template <int NT>
+__device__ __forceinline__ void load_tok(u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts, int kb) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    s.t[nt][0] = gload16(trow[nt] + (int64_t)kb * 128);
-    s.t[nt][1] = gload16(trow[nt] + (int64_t)kb * 128 + 64);
-  }
+  for (int i = 0; i < TokStage<NT>::C; ++i)
+    if (ts.src[i]) tv[i] = gload16(ts.src[i] + (int64_t)kb * 128);
 }
 
-template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void load_slab(Slab<WFMT, NT>& s, const WSrc<WFMT, PACKED>& ws,
-                                          const uint8_t* const (&trow)[NT], int kb) {
-  load_slab_w(s, ws, kb);
-  load_slab_t(s, trow, kb);
+template <int NT>
+__device__ __forceinline__ void store_tok(uint8_t* buf, const u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts) {
+#pragma unroll
+  for (int i = 0; i < TokStage<NT>::C; ++i)
+    if (ts.src[i]) *reinterpret_cast<u32x4*>(buf + ts.dst[i]) = tv[i];
 }
 
+// MFMAs of one slab: weights from registers, token fragments from the staged slab tb.
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const Slab<WFMT, NT>& s,
-                                             const WSrc<WFMT, PACKED>& ws, const float* s_tsc, int kb) {
+__device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws,
+                                             const float* s_tsc, int kb, const uint8_t* tb) {
   float fs[2] = {1.f, 1.f};
   if constexpr (WFMT == MOE_FP8_E4M3) {
     fs[0] = lane_value(ws.fsv[0], kb);
     fs[1] = lane_value(ws.fsv[1], kb);
   }
-  const int r16 = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const v8i bv = {(int)s.t[nt][0].x, (int)s.t[nt][0].y, (int)s.t[nt][0].z, (int)s.t[nt][0].w,
-                    (int)s.t[nt][1].x, (int)s.t[nt][1].y, (int)s.t[nt][1].z, (int)s.t[nt][1].w};
+    const uint8_t* tr = tb + (nt * 16 + r16) * kTokStride + 16 * g4;
+    const u32x4 t0 = *reinterpret_cast<const u32x4*>(tr);
+    const u32x4 t1 = *reinterpret_cast<const u32x4*>(tr + 64);
+    const v8i bv = {(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       v8i av;
@@ -180,37 +195,61 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const Slab<WFMT,
   }
 }
 
-// acc[mt][nt] = promoted sum over all K slabs; one slab in flight while one is consumed.
-// s_tsc holds the pass's token scales, [kb][16*NT].  The scheduling fences keep the
-// loads of the next slab ahead of the consumption of the current one, so the wait
-// before each slab's MFMAs leaves the next slab's loads in flight.
-// On entry, a holds the weights of slab 0 (issued by the caller ahead of its setup).
+// Weight slabs held in registers: 2 (one slab ahead of the one consumed) or 3 (two
+// ahead) where registers allow it: FP4 slabs (16 registers) with at most 3 token tiles.
+template <int WFMT, int NT>
+constexpr int kWeightStages = WFMT == MOE_FP4_E2M1 && NT <= 3 ? 3 : 2;
+
+// acc[mt][nt] = promoted sum over all K slabs.  Weights: kWeightStages register slabs
+// in a ring.  Tokens: two LDS buffers; the slab after the current one is loaded into
+// registers as each step starts and written to the other buffer after the step's
+// MFMAs, and one barrier per step publishes it.  Token loads are issued ahead of the
+// weight loads of the same step, so waiting for them leaves the weights in flight.
+// s_tsc holds the pass's token scales, [kb][16*NT].
+// On entry w0 holds (in flight) the weights of slab 0 and, with three stages, w1 those
+// of slab 1 (when KB > 1).
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws,
-                                         const uint8_t* const (&trow)[NT], const float* s_tsc, int KB,
-                                         Slab<WFMT, NT>& a) {
+__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws, const TokStage<NT>& ts,
+                                         uint8_t* s_tok, const float* s_tsc, int KB, WSlab<WFMT>& w0,
+                                         WSlab<WFMT>& w1) {
+  constexpr int WST = kWeightStages<WFMT, NT>;
+  constexpr int BUF = 16 * NT * kTokStride;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-  Slab<WFMT, NT> b;
-  load_slab_t(a, trow, 0);
-  for (int kb = 0; kb < KB; kb += 2) {
-    load_slab(b, ws, trow, min(kb + 1, KB - 1));
+  u32x4 tv[TokStage<NT>::C];
+  load_tok<NT>(tv, ts, 0);
+  store_tok<NT>(s_tok, tv, ts);
+  __syncthreads();
+  // one K step: `ahead` receives the slab WST - 1 steps after kb
+  auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& ahead) {
+    if (kb + 1 < KB) load_tok<NT>(tv, ts, kb + 1);
+    if (kb + WST - 1 < KB) load_wslab(ahead, ws, kb + WST - 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_slab(acc, a, ws, s_tsc, kb);
+    compute_slab<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, s_tok + (kb & 1) * BUF);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < KB) {
-      load_slab(a, ws, trow, min(kb + 2, KB - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute_slab(acc, b, ws, s_tsc, kb + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    if (kb + 1 < KB) store_tok<NT>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
+    __syncthreads();
+  };
+  if constexpr (WST == 3) {
+    WSlab<WFMT> w2;
+    for (int kb = 0; kb < KB; kb += 3) {
+      step(kb, w0, w2);
+      if (kb + 1 < KB) step(kb + 1, w1, w0);
+      if (kb + 2 < KB) step(kb + 2, w2, w1);
+    }
+  } else {
+    for (int kb = 0; kb < KB; kb += 2) {
+      step(kb, w0, w1);
+      if (kb + 1 < KB) step(kb + 1, w1, w0);
     }
   }
 }
 
 constexpr int kMaxKB = 128;    // K slabs: hidden and intermediate sizes up to 16384
 constexpr int kMaxTok = 6 * 16; // tokens per pass
+constexpr int kTokBytes = 2 * kMaxTok * kTokStride;  // the two token staging buffers
 
 // The pass's token scales into LDS, s_tsc[kb][nt*16 + r16] = scale of this lane's token
 // of tile nt at K slab kb; the 16 (wave, g) lane groups split the K slabs.
@@ -305,56 +344,86 @@ __device__ __forceinline__ bool sentinel_wait(const GemmArgs& p, const uint32_t*
   return ok;
 }
 
-// Token rows of one pass for this lane: column r16 of each 16-token tile.  Rows past
-// the expert's end read the pass's first row (their results are not stored).
+// Where token row mm of group g lives: its bytes (K slab 0), its scale row, and the
+// h / y row its result goes to.
+template <bool GEMM1>
+__device__ __forceinline__ void token_row(const GemmArgs& p, const SegTable& t, int g, int mm, const uint8_t*& row,
+                                          const float*& sc, int& r) {
+  const BatchDims& d = p.d;
+  const bool shared = g == d.E;
+  if (GEMM1 && shared) {
+    const int s = mm / d.T_s, tt = mm - s * d.T_s;
+    row = p.src.x[s] + (int64_t)tt * d.H;
+    sc = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
+    r = d.R + mm;
+  } else {
+    r = shared ? d.R + mm : seg_row(t, d.S, mm);
+    const int stride = GEMM1 ? d.H : d.hstride;
+    row = p.a + (int64_t)r * stride;
+    sc = p.as + (int64_t)r * (stride >> 7);
+  }
+}
+
+// Token rows of one pass for this lane (column r16 of each 16-token tile): scales and
+// output rows (-1 past the expert's end).  Rows past the end read the pass's first
+// row (their results are not stored).
 template <int NT, bool GEMM1>
 __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
-                                          const uint8_t* (&trow)[NT], const float* (&tsc)[NT], int (&orow)[NT]) {
-  const BatchDims& d = p.d;
-  const int lane = threadIdx.x & 63, g4 = lane >> 4, r16 = lane & 15;
-  const bool shared = g == d.E;
+                                          const float* (&tsc)[NT], int (&orow)[NT]) {
+  const int r16 = threadIdx.x & 15;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int m = m0 + nt * 16 + r16;
-    const int mm = m < M ? m : m0;
+    const uint8_t* row;
     int r;
-    if (GEMM1 && shared) {
-      const int s = mm / d.T_s, t = mm - s * d.T_s;
-      trow[nt] = p.src.x[s] + (int64_t)t * d.H + 16 * g4;
-      tsc[nt] = p.src.xs[s] + (int64_t)t * (d.H >> 7);
-      r = d.R + mm;
-    } else {
-      r = shared ? d.R + mm : seg_row(t, d.S, mm);
-      if (GEMM1) {
-        trow[nt] = p.a + (int64_t)r * d.H + 16 * g4;
-        tsc[nt] = p.as + (int64_t)r * (d.H >> 7);
-      } else {
-        trow[nt] = p.a + (int64_t)r * d.hstride + 16 * g4;
-        tsc[nt] = p.as + (int64_t)r * (d.hstride >> 7);
-      }
-    }
+    token_row<GEMM1>(p, t, g, m < M ? m : m0, row, tsc[nt], r);
     orow[nt] = m < M ? r : -1;
+  }
+}
+
+// This thread's chunks of the pass's token staging (TokStage).
+template <int NT, bool GEMM1>
+__device__ __forceinline__ void stage_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
+                                           TokStage<NT>& ts) {
+#pragma unroll
+  for (int i = 0; i < TokStage<NT>::C; ++i) {
+    const int c = threadIdx.x + 256 * i, row = c >> 3;
+    ts.src[i] = nullptr;
+    ts.dst[i] = row * kTokStride + 16 * (c & 7);
+    if (row < 16 * NT) {
+      const int m = m0 + row;
+      const uint8_t* rp;
+      const float* sc;
+      int r;
+      token_row<GEMM1>(p, t, g, m < M ? m : m0, rp, sc, r);
+      ts.src[i] = rp + 16 * (c & 7);
+    }
   }
 }
 
 // ------------------------------------------------------------------ GEMM1
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
-                                           int g, int nb, int M, int m0, float (*s_amax)[kMaxTok], float* s_tsc) {
+                                           int g, int nb, int M, int m0, float (*s_amax)[kMaxTok], float* s_tsc,
+                                           uint8_t* s_tok) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const uint8_t* trow[NT];
+  const int KB = d.H >> 7;
   const float* tsc[NT];
   int orow[NT];
-  Slab<WFMT, NT> slab0;
-  load_slab_w(slab0, ws, 0);  // the first weight slab is in flight during the pass setup
+  TokStage<NT> ts;
+  WSlab<WFMT> w0, w1;
+  // the first weight slabs are in flight during the pass setup
+  load_wslab(w0, ws, 0);
+  if (kWeightStages<WFMT, NT> == 3 && KB > 1) load_wslab(w1, ws, 1);
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, true>(p, t, g, M, m0, trow, tsc, orow);
-  stage_token_scales<NT>(s_tsc, tsc, d.H >> 7);
+  pass_rows<NT, true>(p, t, g, M, m0, tsc, orow);
+  stage_rows<NT, true>(p, t, g, M, m0, ts);
+  stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
-  mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, d.H >> 7, slab0);
+  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0, w1);
 
   // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
   float hv[2][NT][4];
@@ -400,7 +469,7 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
 // all of the group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
 __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item, float (*s_amax)[kMaxTok],
-                                           float* s_tsc, SegTable& seg) {
+                                           float* s_tsc, uint8_t* s_tok, SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -453,12 +522,12 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
   for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
-      case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
-      case 5: if constexpr (NTMAX >= 5) gemm1_pass<WFMT, PACKED, 5>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
-      default: if constexpr (NTMAX >= 6) gemm1_pass<WFMT, PACKED, 6>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc); break;
+      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      case 5: if constexpr (NTMAX >= 5) gemm1_pass<WFMT, PACKED, 5>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      default: if constexpr (NTMAX >= 6) gemm1_pass<WFMT, PACKED, 6>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
     }
   }
 }
@@ -471,6 +540,7 @@ template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs da, int ndisp, int chunks) {
   __shared__ float s_amax[4][kMaxTok];
   __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ SegTable seg;
   static_assert(sizeof(DispatchSmem) <= sizeof(s_tsc), "the dispatch chunk borrows s_tsc");
   if ((int)blockIdx.x < ndisp) {
@@ -480,26 +550,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs 
   }
   int g, nb;
   work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, (int)blockIdx.x - ndisp, g, nb);
-  gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, seg);
+  gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg);
 }
 
 // ------------------------------------------------------------------ GEMM2
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
-                                           int g, int rb, bool active, int K, int M, int m0, float* s_tsc) {
+                                           int g, int rb, bool active, int K, int M, int m0, float* s_tsc,
+                                           uint8_t* s_tok) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
-  const uint8_t* trow[NT];
+  const int KB = K >> 7;
   const float* tsc[NT];
   int orow[NT];
-  Slab<WFMT, NT> slab0;
-  if (active) load_slab_w(slab0, ws, 0);  // the first weight slab is in flight during the pass setup
+  TokStage<NT> ts;
+  WSlab<WFMT> w0, w1;
+  // the first weight slabs are in flight during the pass setup
+  load_wslab(w0, ws, 0);
+  if (kWeightStages<WFMT, NT> == 3 && KB > 1) load_wslab(w1, ws, 1);
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, false>(p, t, g, M, m0, trow, tsc, orow);
-  stage_token_scales<NT>(s_tsc, tsc, K >> 7);
+  pass_rows<NT, false>(p, t, g, M, m0, tsc, orow);
+  stage_rows<NT, false>(p, t, g, M, m0, ts);
+  stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
-  if (active) mainloop<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, K >> 7, slab0);
+  // a wave past a ragged end of H repeats the last tile's rows and stores nothing
+  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0, w1);
   __syncthreads();  // s_tsc is reused by the next pass
   if (!active) return;
 #pragma unroll
@@ -517,7 +593,8 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
 // One GEMM2 work item: output rows nb*256 .. +255 of expert group g, over all of the
 // group's rows.  Every thread of the workgroup calls it.
 template <int NTMAX, int WFMT, bool PACKED>
-__device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item, float* s_tsc, SegTable& seg) {
+__device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item, float* s_tsc, uint8_t* s_tok,
+                                           SegTable& seg) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -527,7 +604,8 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
     nb /= p.sh_chunks;
   }
   const int rb0 = nb * 256 + 64 * wave;
-  const bool active = rb0 < d.H;      // a ragged last tile: such waves only help stage scales
+  const bool active = rb0 < d.H;      // a ragged last tile: such waves compute rows rb.. again
+
   const int rb = active ? rb0 : d.H - 64;
   const bool shared = g == d.E;
   const int K = shared ? d.Ish : d.I, KB = K >> 7;
@@ -564,12 +642,12 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
   for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
-      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
-      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
-      case 4: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
-      case 5: if constexpr (NTMAX >= 5) gemm2_pass<WFMT, PACKED, 5>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
-      default: if constexpr (NTMAX >= 6) gemm2_pass<WFMT, PACKED, 6>(p, ws, seg, g, rb, active, K, me, m0, s_tsc); break;
+      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      case 4: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      case 5: if constexpr (NTMAX >= 5) gemm2_pass<WFMT, PACKED, 5>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      default: if constexpr (NTMAX >= 6) gemm2_pass<WFMT, PACKED, 6>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
     }
   }
 }
@@ -577,11 +655,12 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ SegTable seg;
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
   work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, blockIdx.x, g, nb);
-  gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, seg);
+  gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, s_tok, seg);
 }
 
 // ------------------------------------------------------------------ persistent
@@ -620,6 +699,7 @@ template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
   __shared__ float s_amax[4][kMaxTok];
   __shared__ float s_tsc[kMaxKB * kMaxTok];
+  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ int s_item, s_go;
   __shared__ SegTable seg;
   const int q = a.per_xcd ? (blockIdx.x & 7) : 0, step = a.per_xcd ? 8 : 1;
@@ -634,7 +714,7 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
     const int kind = decode_item(a, q, step, i, g, nb);
     if (kind == 0) break;  // uniform over the workgroup
     if (kind == 1) {
-      gemm1_item<NTMAX, WFMT, PACKED>(a.g1, g, nb, s_amax, s_tsc, seg);
+      gemm1_item<NTMAX, WFMT, PACKED>(a.g1, g, nb, s_amax, s_tsc, s_tok, seg);
       __syncthreads();  // every wave's h stores are done
       if (threadIdx.x == 0) __hip_atomic_fetch_add(done1 + g, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -652,7 +732,7 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
         if (!s_go) atomicOr(a.g1.err, MOE_DEVERR_TIMEOUT);
       }
       __syncthreads();
-      if (s_go) gemm2_item<NTMAX, WFMT, PACKED>(a.g2, g, nb, s_tsc, seg);
+      if (s_go) gemm2_item<NTMAX, WFMT, PACKED>(a.g2, g, nb, s_tsc, s_tok, seg);
     }
     __syncthreads();  // s_item, s_go and the LDS tables are free again
   }
