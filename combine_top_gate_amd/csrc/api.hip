@@ -102,12 +102,13 @@ moe_status check_config(const moe_config* c) {
   if (c->n_src < 1 || c->n_src > MOE_MAX_SRC)
     return fail(MOE_ERR_INVALID_ARG, "n_src %d outside 1..%d", c->n_src, MOE_MAX_SRC);
   if (c->max_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "max_tokens %d < 0", c->max_tokens);
-  if (c->hidden <= 0 || c->hidden % 128)
-    return fail(MOE_ERR_INVALID_ARG, "hidden %d is not a positive multiple of 128", c->hidden);
-  if (c->inter <= 0 || c->inter % 128)
-    return fail(MOE_ERR_INVALID_ARG, "inter %d is not a positive multiple of 128", c->inter);
-  if (c->shared_inter < 0 || c->shared_inter % 128)
-    return fail(MOE_ERR_INVALID_ARG, "shared_inter %d is not a multiple of 128", c->shared_inter);
+  if (c->hidden <= 0 || c->hidden % 128 || c->hidden > MOE_MAX_DIM)
+    return fail(MOE_ERR_INVALID_ARG, "hidden %d is not a positive multiple of 128 up to %d", c->hidden, MOE_MAX_DIM);
+  if (c->inter <= 0 || c->inter % 128 || c->inter > MOE_MAX_DIM)
+    return fail(MOE_ERR_INVALID_ARG, "inter %d is not a positive multiple of 128 up to %d", c->inter, MOE_MAX_DIM);
+  if (c->shared_inter < 0 || c->shared_inter % 128 || c->shared_inter > MOE_MAX_DIM)
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter %d is not a multiple of 128 up to %d", c->shared_inter,
+                MOE_MAX_DIM);
   if (c->n_experts < 1 || c->n_experts > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_INVALID_ARG, "n_experts %d outside 1..%d", c->n_experts, MOE_MAX_EXPERTS);
   if (c->topk < 1 || c->topk > MOE_MAX_TOPK || c->topk > c->n_experts)
@@ -457,7 +458,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   const int groups = d.E + (d.Ish ? 1 : 0);
   const int items = d.E * ea.nb1_r + ea.nb1_s * g.sh_chunks + d.E * ea.nb2 + (d.Ish ? ea.nb2 * g.sh_chunks : 0);
   (void)groups;
-  const int per_cu = std::max(1, experts_lowp_blocks_per_cu(cf.weight, packed, nt));
+  const int per_cu = std::max(1, experts_lowp_blocks_per_cu(cf.weight, packed, nt, std::max(d.H, d.hstride) / 128));
   int grid = std::min(items, per_cu * c->n_cu);
   if (ea.per_xcd) grid = std::max(8, grid / 8 * 8);
   HIP_TRY(launch_experts_lowp(ea, cf.weight, packed, nt, grid, stream));

@@ -31,6 +31,8 @@
 // k = 64+16g..64+16g+15 in bytes 16..31; an FP4 operand holds k = 32g..32g+31 as
 // nibbles (element 2i in the low nibble of byte i) and lane l's e8m0 scale covers
 // exactly those 32 k.  The result's lane l, register i is row 4g+i, column l%16.
+#include <algorithm>
+
 #include "dispatch_chunk.h"
 #include "kernels.h"
 #include "pack_layout.h"
@@ -136,27 +138,28 @@ __device__ __forceinline__ void load_wslab(WSlab<WFMT>& s, const WSrc<WFMT, PACK
 // B-operand reads (16 rows x 4 lane groups per instruction) free of bank conflicts.
 constexpr int kTokStride = 144;
 
-// This thread's share of staging one K slab: chunk c = threadIdx.x + 256 i is bytes
-// 16 (c % 8) .. +15 of token row c / 8.
+// This thread's share of staging one K slab: chunk c = (threadIdx.x + 256 i) mod
+// (16 NT 8) is bytes 16 (c % 8) .. +15 of token row c / 8.  Threads past the last
+// chunk repeat one (same bytes to the same place), so the loads and stores carry no
+// per-thread condition: a divergent branch around them would make the compiler wait
+// for every load in flight, weights included, before the store.
 template <int NT>
 struct TokStage {
   static constexpr int C = (NT * 16 * 8 + 255) / 256;
-  const uint8_t* src[C];  // the chunk at K slab 0, or null (no chunk)
+  const uint8_t* src[C];  // the chunk at K slab 0
   int dst[C];             // byte offset in a staging buffer
 };
 
 template <int NT>
 __device__ __forceinline__ void load_tok(u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts, int kb) {
 #pragma unroll
-  for (int i = 0; i < TokStage<NT>::C; ++i)
-    if (ts.src[i]) tv[i] = gload16(ts.src[i] + (int64_t)kb * 128);
+  for (int i = 0; i < TokStage<NT>::C; ++i) tv[i] = gload16(ts.src[i] + (int64_t)kb * 128);
 }
 
 template <int NT>
 __device__ __forceinline__ void store_tok(uint8_t* buf, const u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts) {
 #pragma unroll
-  for (int i = 0; i < TokStage<NT>::C; ++i)
-    if (ts.src[i]) *reinterpret_cast<u32x4*>(buf + ts.dst[i]) = tv[i];
+  for (int i = 0; i < TokStage<NT>::C; ++i) *reinterpret_cast<u32x4*>(buf + ts.dst[i]) = tv[i];
 }
 
 // MFMAs of one slab: weights from registers, token fragments from the staged slab tb.
@@ -192,27 +195,21 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT
       acc[mt][nt][2] = fmaf(r[2], sc, acc[mt][nt][2]);
       acc[mt][nt][3] = fmaf(r[3], sc, acc[mt][nt][3]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // one token tile's fragments live at a time
   }
 }
 
-// Weight slabs held in registers: 2 (one slab ahead of the one consumed) or 3 (two
-// ahead) where registers allow it: FP4 slabs (16 registers) with at most 3 token tiles.
-template <int WFMT, int NT>
-constexpr int kWeightStages = WFMT == MOE_FP4_E2M1 && NT <= 3 ? 3 : 2;
-
-// acc[mt][nt] = promoted sum over all K slabs.  Weights: kWeightStages register slabs
-// in a ring.  Tokens: two LDS buffers; the slab after the current one is loaded into
-// registers as each step starts and written to the other buffer after the step's
-// MFMAs, and one barrier per step publishes it.  Token loads are issued ahead of the
-// weight loads of the same step, so waiting for them leaves the weights in flight.
-// s_tsc holds the pass's token scales, [kb][16*NT].
-// On entry w0 holds (in flight) the weights of slab 0 and, with three stages, w1 those
-// of slab 1 (when KB > 1).
+// acc[mt][nt] = promoted sum over all K slabs.  Weights: two register slabs, the next
+// one in flight while the current one is consumed (a third slab costs more in spills
+// than it gains, measured for FP4 and FP8).  Tokens: two LDS buffers; the slab after
+// the current one is loaded into registers as each step starts and written to the
+// other buffer after the step's MFMAs, and one barrier per step publishes it.  Token
+// loads are issued ahead of the weight loads of the same step, so waiting for them
+// leaves the weights in flight.  s_tsc holds the pass's token scales, [kb][16*NT].
+// On entry w0 holds (in flight) the weights of slab 0.
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws, const TokStage<NT>& ts,
-                                         uint8_t* s_tok, const float* s_tsc, int KB, WSlab<WFMT>& w0,
-                                         WSlab<WFMT>& w1) {
-  constexpr int WST = kWeightStages<WFMT, NT>;
+                                         uint8_t* s_tok, const float* s_tsc, int KB, WSlab<WFMT>& w0) {
   constexpr int BUF = 16 * NT * kTokStride;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -222,34 +219,34 @@ __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PAC
   load_tok<NT>(tv, ts, 0);
   store_tok<NT>(s_tok, tv, ts);
   __syncthreads();
-  // one K step: `ahead` receives the slab WST - 1 steps after kb
-  auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& ahead) {
+  // one K step: `next` receives the weights of slab kb + 1
+  auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& next) {
     if (kb + 1 < KB) load_tok<NT>(tv, ts, kb + 1);
-    if (kb + WST - 1 < KB) load_wslab(ahead, ws, kb + WST - 1);
+    if (kb + 1 < KB) load_wslab(next, ws, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute_slab<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, s_tok + (kb & 1) * BUF);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 1 < KB) store_tok<NT>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
     __syncthreads();
   };
-  if constexpr (WST == 3) {
-    WSlab<WFMT> w2;
-    for (int kb = 0; kb < KB; kb += 3) {
-      step(kb, w0, w2);
-      if (kb + 1 < KB) step(kb + 1, w1, w0);
-      if (kb + 2 < KB) step(kb + 2, w2, w1);
-    }
-  } else {
-    for (int kb = 0; kb < KB; kb += 2) {
-      step(kb, w0, w1);
-      if (kb + 1 < KB) step(kb + 1, w1, w0);
-    }
+  WSlab<WFMT> w1;
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, w0, w1);
+    if (kb + 1 < KB) step(kb + 1, w1, w0);
   }
 }
 
-constexpr int kMaxKB = 128;    // K slabs: hidden and intermediate sizes up to 16384
-constexpr int kMaxTok = 6 * 16; // tokens per pass
-constexpr int kTokBytes = 2 * kMaxTok * kTokStride;  // the two token staging buffers
+constexpr int kMaxKB = MOE_MAX_DIM / 128;  // K slabs (the weight-scale lanes hold 128)
+constexpr int kMaxTok = 6 * 16;            // tokens per pass
+
+// Dynamic LDS of the decode GEMM kernels, sized per launch for K slabs and at most
+// NTMAX token tiles per pass: the pass's token scales [KB][16*NT] fp32, then the two
+// token staging buffers: a few tens of KB instead of the worst case.
+extern __shared__ __align__(16) uint8_t g_lds[];
+__host__ __device__ constexpr int lds_tsc_bytes(int KB, int ntmax) { return (KB * 16 * ntmax * 4 + 15) / 16 * 16; }
+__host__ __device__ constexpr int lds_bytes(int KB, int ntmax) {
+  return lds_tsc_bytes(KB, ntmax) + 2 * 16 * ntmax * kTokStride;
+}
 
 // The pass's token scales into LDS, s_tsc[kb][nt*16 + r16] = scale of this lane's token
 // of tile nt at K slab kb; the 16 (wave, g) lane groups split the K slabs.
@@ -387,17 +384,14 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, const SegTable& t,
                                            TokStage<NT>& ts) {
 #pragma unroll
   for (int i = 0; i < TokStage<NT>::C; ++i) {
-    const int c = threadIdx.x + 256 * i, row = c >> 3;
-    ts.src[i] = nullptr;
+    const int c = (threadIdx.x + 256 * i) % (16 * NT * 8), row = c >> 3;
     ts.dst[i] = row * kTokStride + 16 * (c & 7);
-    if (row < 16 * NT) {
-      const int m = m0 + row;
-      const uint8_t* rp;
-      const float* sc;
-      int r;
-      token_row<GEMM1>(p, t, g, m < M ? m : m0, rp, sc, r);
-      ts.src[i] = rp + 16 * (c & 7);
-    }
+    const int m = m0 + row;
+    const uint8_t* rp;
+    const float* sc;
+    int r;
+    token_row<GEMM1>(p, t, g, m < M ? m : m0, rp, sc, r);
+    ts.src[i] = rp + 16 * (c & 7);
   }
 }
 
@@ -413,17 +407,15 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
   const float* tsc[NT];
   int orow[NT];
   TokStage<NT> ts;
-  WSlab<WFMT> w0, w1;
-  // the first weight slabs are in flight during the pass setup
-  load_wslab(w0, ws, 0);
-  if (kWeightStages<WFMT, NT> == 3 && KB > 1) load_wslab(w1, ws, 1);
+  WSlab<WFMT> w0;
+  load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
   pass_rows<NT, true>(p, t, g, M, m0, tsc, orow);
   stage_rows<NT, true>(p, t, g, M, m0, ts);
   stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
-  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0, w1);
+  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
 
   // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
   float hv[2][NT][4];
@@ -539,13 +531,13 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs da, int ndisp, int chunks) {
   __shared__ float s_amax[4][kMaxTok];
-  __shared__ float s_tsc[kMaxKB * kMaxTok];
-  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ SegTable seg;
-  static_assert(sizeof(DispatchSmem) <= sizeof(s_tsc), "the dispatch chunk borrows s_tsc");
+  float* s_tsc = reinterpret_cast<float*>(g_lds);
+  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.H >> 7, NTMAX);
   if ((int)blockIdx.x < ndisp) {
+    // the launch sizes the dynamic LDS to hold a DispatchSmem as well
     const int b = blockIdx.x;
-    if (b < da.S * chunks) dispatch_chunk(da, b / chunks, b % chunks, chunks, *reinterpret_cast<DispatchSmem*>(s_tsc));
+    if (b < da.S * chunks) dispatch_chunk(da, b / chunks, b % chunks, chunks, *reinterpret_cast<DispatchSmem*>(g_lds));
     return;
   }
   int g, nb;
@@ -564,10 +556,8 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
   const float* tsc[NT];
   int orow[NT];
   TokStage<NT> ts;
-  WSlab<WFMT> w0, w1;
-  // the first weight slabs are in flight during the pass setup
-  load_wslab(w0, ws, 0);
-  if (kWeightStages<WFMT, NT> == 3 && KB > 1) load_wslab(w1, ws, 1);
+  WSlab<WFMT> w0;
+  load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
   pass_rows<NT, false>(p, t, g, M, m0, tsc, orow);
   stage_rows<NT, false>(p, t, g, M, m0, ts);
@@ -575,7 +565,7 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
   __syncthreads();
   v4f acc[4][NT];
   // a wave past a ragged end of H repeats the last tile's rows and stores nothing
-  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0, w1);
+  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
   __syncthreads();  // s_tsc is reused by the next pass
   if (!active) return;
 #pragma unroll
@@ -654,9 +644,9 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
 
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
-  __shared__ float s_tsc[kMaxKB * kMaxTok];
-  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ SegTable seg;
+  float* s_tsc = reinterpret_cast<float*>(g_lds);
+  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.hstride >> 7, NTMAX);
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
   work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, blockIdx.x, g, nb);
@@ -698,10 +688,10 @@ __device__ __forceinline__ int decode_item(const ExpertsArgs& a, int q, int step
 template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
   __shared__ float s_amax[4][kMaxTok];
-  __shared__ float s_tsc[kMaxKB * kMaxTok];
-  __shared__ __align__(16) uint8_t s_tok[kTokBytes];
   __shared__ int s_item, s_go;
   __shared__ SegTable seg;
+  float* s_tsc = reinterpret_cast<float*>(g_lds);
+  uint8_t* s_tok = g_lds + lds_tsc_bytes(max(a.g1.d.H, a.g1.d.hstride) >> 7, NTMAX);
   const int q = a.per_xcd ? (blockIdx.x & 7) : 0, step = a.per_xcd ? 8 : 1;
   uint32_t* head = a.sched + q;
   uint32_t* exits = a.sched + 8;
@@ -757,14 +747,19 @@ hipError_t launch1(const GemmArgs& a, int nt, const DispatchArgs* fused, hipStre
     ndisp = (da.S * chunks + 7) / 8 * 8;
   }
   const dim3 grid(ndisp + a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
+  const int KB = a.d.H >> 7;
+  auto lds = [&](int ntmax) {
+    const int b = lds_bytes(KB, ntmax);
+    return (size_t)(ndisp && b < (int)sizeof(DispatchSmem) ? (int)sizeof(DispatchSmem) : b);
+  };
   if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
+    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, lds(2), st, a, da, ndisp, chunks);
   else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
+    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, lds(3), st, a, da, ndisp, chunks);
   else if (nt == 4 || WFMT != MOE_FP4_E2M1)
-    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
+    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, lds(4), st, a, da, ndisp, chunks);
   else
-    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a, da, ndisp, chunks);
+    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, lds(5), st, a, da, ndisp, chunks);
   return hipGetLastError();
 }
 
@@ -772,38 +767,40 @@ template <int WFMT, bool PACKED>
 hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   const int nbh = (a.d.H + 255) >> 8;
   const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh * a.sh_chunks : 0)), block(256);
+  const int KB = a.d.hstride >> 7;
   if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, lds_bytes(KB, 2), st, a);
   else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, lds_bytes(KB, 3), st, a);
   else if (nt == 4 || WFMT != MOE_FP4_E2M1)
-    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, lds_bytes(KB, 4), st, a);
   else
-    hipLaunchKernelGGL((k_gemm2_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, lds_bytes(KB, 5), st, a);
   return hipGetLastError();
 }
 
 template <int WFMT, bool PACKED>
 hipError_t launch_experts(const ExpertsArgs& a, int nt, int grid, hipStream_t st) {
+  const int KB = std::max(a.g1.d.H, a.g1.d.hstride) >> 7;
   if (nt <= 2)
-    hipLaunchKernelGGL((k_experts_lowp<2, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_experts_lowp<2, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 2), st, a);
   else if (nt == 3)
-    hipLaunchKernelGGL((k_experts_lowp<3, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_experts_lowp<3, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 3), st, a);
   else
-    hipLaunchKernelGGL((k_experts_lowp<4, WFMT, PACKED>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_experts_lowp<4, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 4), st, a);
   return hipGetLastError();
 }
 
 template <int WFMT, bool PACKED>
-int experts_blocks_per_cu(int nt) {
+int experts_blocks_per_cu(int nt, int KB) {
   int n = 0;
   hipError_t e;
   if (nt <= 2)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<2, WFMT, PACKED>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<2, WFMT, PACKED>, 256, lds_bytes(KB, 2));
   else if (nt == 3)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<3, WFMT, PACKED>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<3, WFMT, PACKED>, 256, lds_bytes(KB, 3));
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<4, WFMT, PACKED>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_experts_lowp<4, WFMT, PACKED>, 256, lds_bytes(KB, 4));
   return e == hipSuccess ? n : 0;
 }
 
@@ -818,12 +815,12 @@ hipError_t launch_experts_lowp(const ExpertsArgs& a, int weight_fmt, int packed,
                 : launch_experts<MOE_FP8_E4M3, false>(a, tok_tiles, grid, st);
 }
 
-int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles) {
+int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles, int k_slabs) {
   if (weight_fmt == MOE_FP4_E2M1)
-    return packed ? experts_blocks_per_cu<MOE_FP4_E2M1, true>(tok_tiles)
-                  : experts_blocks_per_cu<MOE_FP4_E2M1, false>(tok_tiles);
-  return packed ? experts_blocks_per_cu<MOE_FP8_E4M3, true>(tok_tiles)
-                : experts_blocks_per_cu<MOE_FP8_E4M3, false>(tok_tiles);
+    return packed ? experts_blocks_per_cu<MOE_FP4_E2M1, true>(tok_tiles, k_slabs)
+                  : experts_blocks_per_cu<MOE_FP4_E2M1, false>(tok_tiles, k_slabs);
+  return packed ? experts_blocks_per_cu<MOE_FP8_E4M3, true>(tok_tiles, k_slabs)
+                : experts_blocks_per_cu<MOE_FP8_E4M3, false>(tok_tiles, k_slabs);
 }
 
 hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st,

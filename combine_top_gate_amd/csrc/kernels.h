@@ -81,7 +81,7 @@ struct ExpertsArgs {
 };
 hipError_t launch_experts_lowp(const ExpertsArgs& a, int weight_fmt, int packed, int tok_tiles, int grid,
                                hipStream_t st);
-int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles);
+int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles, int k_slabs);
 // LDS-tiled GEMMs for large expert row counts (FP8 weights; gemm_tiled.hip): a plan
 // kernel, then GEMM1 and GEMM2 on persistent grids fed by atomic work counters.
 struct TiledArgs {

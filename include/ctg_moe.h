@@ -87,6 +87,7 @@ extern "C" {
 #define MOE_MAX_SRC 32      /* simulated source ranks */
 #define MOE_MAX_EXPERTS 256 /* local routed experts */
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_DIM 16384   /* hidden, inter and shared_inter: multiples of 128 up to this */
 
 typedef enum {
   MOE_OK = 0,

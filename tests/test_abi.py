@@ -40,7 +40,8 @@ def _create(lib, cfg):
 
 
 @pytest.mark.parametrize("field,value,needle", [
-    ("hidden", 100, "hidden"), ("inter", 0, "inter"), ("n_src", 0, "n_src"),
+    ("hidden", 100, "hidden"), ("hidden", 16384 + 128, "hidden"), ("inter", 0, "inter"),
+    ("inter", 16384 + 128, "inter"), ("n_src", 0, "n_src"),
     ("n_src", 33, "n_src"), ("topk", 0, "topk"), ("n_experts", 300, "n_experts"),
     ("shared_inter", 64, "shared_inter"), ("max_tokens", -1, "max_tokens"),
     ("out", binding.MOE_F32, "dtype"), ("weight", binding.MOE_F32, "dtype"),
