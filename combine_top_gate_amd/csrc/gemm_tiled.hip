@@ -8,16 +8,21 @@
 // With hundreds to thousands of rows per expert the layer is bound by MFMA, not by the
 // weight stream, so both operands are reused from LDS: a workgroup computes a tile of
 // 128 token rows x 256 weight rows; per 128-deep K slab it stages the token slab
-// (16 KB) and the weight slab (32 KB) in LDS (double buffered, loads for slab k+1 in
-// flight while slab k is multiplied), and each of its 8 waves multiplies 64 tokens x
-// 64 weight rows (16 MFMAs per slab), promoting every MFMA result with
-// (weight scale x token scale).  GEMM1's 256 weight rows are 128 gate + the matching
+// (16 KB), the weight slab (32 KB) and their scales in LDS, and each of its 8 waves
+// multiplies 64 tokens x 64 weight rows (16 MFMAs per slab), promoting every MFMA
+// result with (weight scale x token scale).  The slabs go from memory straight into
+// a ring of three LDS stages (global_load_lds), two slabs ahead of the one being
+// multiplied, with no staging registers; one barrier per slab.  GEMM1's 256 weight rows are 128 gate + the matching
 // 128 up rows, so SwiGLU and the per-128-column requantisation stay in the epilogue.
 //
-// Experts' loads are uneven (skewed routing), so work is a flat list of
-// (expert, 128-row token tile, column block) items built on the device from the row
-// counts (k_plan) and handed out by an atomic counter to a persistent grid: a
-// workgroup that finishes early takes the next item, whichever expert it belongs to.
+// Work items are (expert, 128-row token tile, column block), grouped into super-tiles
+// of 4 token tiles x 8 column blocks of one expert, built on the device from the row
+// counts (k_plan).  An XCD's 32 CUs work on one super-tile at a time, so its token
+// tiles and weight blocks are read once into that XCD's L2 and reused 8 and 4 times
+// (a 4.8x cut in L2 fill traffic against items spread over all XCDs).  Each XCD has
+// its own queue of super-tiles (every 8th one), served by an atomic counter to a
+// persistent grid; when its queue is empty, a workgroup takes items from the next
+// XCD's queue, so skewed expert loads still balance across the GPU.
 #include "kernels.h"
 #include "pack_layout.h"
 
@@ -29,7 +34,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 128;            // token rows per tile
 constexpr int BN = 256;            // weight rows per tile
 constexpr int kThreads = 512;      // 8 waves: 2 (token halves) x 4 (weight quarters)
-constexpr int kStride = 144;       // LDS bytes per staged 128-byte row (+16 against bank conflicts)
+constexpr int kStride = 128;       // LDS bytes per staged 128-byte row (16-byte chunks swizzled)
 constexpr int kAPieces = BM * 8;   // 16-byte pieces of a token slab
 constexpr int kWPieces = BN * 8;   // 16-byte pieces of a weight slab
 constexpr int kALd = kAPieces / kThreads;  // 2
@@ -38,21 +43,63 @@ constexpr int kWLd = kWPieces / kThreads;  // 4
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const GLOBAL u32x4*)p; }
 __device__ __forceinline__ float gloadf(const float* p) { return *(const GLOBAL float*)p; }
 
-struct Tiles {
-  uint8_t a[2][BM * kStride];
-  uint8_t w[2][BN * kStride];
-  float sx[2][BM];          // token scales of the staged slab
-  float sw[2][2];           // weight scales of the staged slab (two 128-row blocks)
+// Staged rows keep their eight 16-byte chunks in swizzled order: chunk c of row r sits at
+// chunk c ^ ((r >> 1) & 7).  A B-operand read (16 consecutive rows, one chunk) then
+// touches 16 distinct groups of 4 banks, and a store of two rows (16 lanes) fills the
+// two halves of the 64 banks: both conflict-free.
+__device__ __forceinline__ int swz(int r, int c) { return r * kStride + ((c ^ ((r >> 1) & 7)) << 4); }
+
+#define LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(const LDS_AS uint8_t*)p; }
+
+// Memory -> LDS without registers: lane l of the wave writes its 16 (4) bytes at
+// dst + 16 l (4 l), dst wave-uniform; counted by vmcnt like any load.  Issued from
+// assembly: the compiler cannot tell which LDS stage such a load fills, and if it knew
+// of them it would wait for every one in flight (later stages included) before any
+// LDS read.  It does not need to know: the data is read only after wait7_barrier() /
+// wait0_barrier(), whose memory clobbers also keep every LDS access on its side.
+// No register is written, so nothing of the load is left to land in a register.
+__device__ __forceinline__ void dma16(const void* src, const void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, const void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+// Wait until at most 7 (or 0) of this wave's memory loads are in flight, then the
+// workgroup barrier, in one block: __syncthreads() would also wait for every pending
+// memory-to-LDS load, and a bare barrier intrinsic would let the compiler move memory
+// operations across it.  The memory clobber keeps both orders.
+__device__ __forceinline__ void wait7_barrier() { asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait0_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+
+
+constexpr int kStages = 3;  // LDS ring depth
+
+struct __align__(16) Tiles {
+  uint8_t a[kStages][BM * kStride];
+  uint8_t w[kStages][BN * kStride];
+  float sx[kStages][BM];    // token scales of the staged slab
+  float sw[kStages][64];    // weight scales of the staged slab (two 128-row blocks) in [0..1]
+  float sdummy[64];         // where the idle lanes' scale loads go
   float amax[4][BM];        // GEMM1: per weight quarter, per token row
   int pre[MOE_MAX_SRC + 1]; // expert row segments (see gemm_lowp.hip SegTable)
   int row0[MOE_MAX_SRC];
   int item;
 };
 
-// k_plan: per group g, tiles[g] = ceil(rows/BM); item prefix for GEMM1 and GEMM2.
-// plan layout: [0] total GEMM1 items, [1] total GEMM2 items, [2 + g] GEMM1 item start
-// of group g, [2 + 260 + g] GEMM2 item start, [2 + 520 + g] rows of g; [522 + 260] the
-// two work counters (zeroed here for the launches that follow).
+constexpr int kSTM = 4, kSTN = 8;  // super-tile: token tiles x column blocks
+constexpr int kSlots = kSTM * kSTN;
+constexpr int kXcds = 8;
+
+// k_plan: per group g, tiles = ceil(rows/BM) token tiles, and its super-tiles for GEMM1
+// and GEMM2.  plan layout: [0] GEMM1 super-tiles, [1] GEMM2 super-tiles, [2 + g]
+// first GEMM1 super-tile of group g, [2 + 260 + g] first GEMM2 super-tile, [2 + 520 +
+// g] rows of g; from [2 + 780] the 8 GEMM1 and 8 GEMM2 queue counters (zeroed here for
+// the launches that follow).
 constexpr int kPlanG1 = 2, kPlanG2 = 2 + 260, kPlanRows = 2 + 520, kPlanCtr = 2 + 780;
 
 __global__ __launch_bounds__(256) void k_plan(TiledArgs t) {
@@ -71,20 +118,19 @@ __global__ __launch_bounds__(256) void k_plan(TiledArgs t) {
   if (threadIdx.x == 0) {
     int a1 = 0, a2 = 0;
     for (int g = 0; g < nG; ++g) {
-      const int tiles = (s_rows[g] + BM - 1) / BM;
+      const int stm = (s_rows[g] + BM * kSTM - 1) / (BM * kSTM);
       t.plan[kPlanG1 + g] = a1;
       t.plan[kPlanG2 + g] = a2;
       t.plan[kPlanRows + g] = s_rows[g];
-      a1 += tiles * (g < d.E ? t.nb1_r : t.nb1_s);
-      a2 += tiles * t.nb2;
+      a1 += stm * (((g < d.E ? t.nb1_r : t.nb1_s) + kSTN - 1) / kSTN);
+      a2 += stm * ((t.nb2 + kSTN - 1) / kSTN);
     }
     t.plan[kPlanG1 + nG] = a1;
     t.plan[kPlanG2 + nG] = a2;
     t.plan[0] = a1;
     t.plan[1] = a2;
-    t.plan[kPlanCtr] = 0;
-    t.plan[kPlanCtr + 1] = 0;
   }
+  if (threadIdx.x < 2 * kXcds) t.plan[kPlanCtr + threadIdx.x] = 0;
 }
 
 __device__ __forceinline__ void segments(const GemmArgs& p, int g, Tiles& T) {
@@ -126,14 +172,16 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
   const int seg = d.T_s * d.k;
   (void)seg;
 
-  // ---- where this thread's slab pieces come from
+  // ---- this thread's DMA sources.  Instruction i of wave w fills the 1 KB at
+  // 16 * ((w * n + i) * 64 + lane) of a stage buffer: chunk p = (w * n + i) * 64 + lane
+  // is physical chunk p % 8 of row p / 8, which holds that row's logical chunk
+  // (p % 8) ^ ((row >> 1) & 7) (the swizzle of swz()).
   const uint8_t* asrc[kALd];
-  const float* tscp = nullptr;
-  int adst[kALd];
 #pragma unroll
   for (int i = 0; i < kALd; ++i) {
-    const int q = tid + kThreads * i;
-    const int r = q >> 3;               // tile row
+    const int q = (wave * kALd + i) * 64 + lane;
+    const int r = q >> 3;
+    const int c = (q & 7) ^ ((r >> 1) & 7);
     const int m = min(m0 + r, M - 1);   // rows past the end repeat the last one (not stored)
     const uint8_t* rowp;
     if (GEMM1 && shared) {
@@ -143,76 +191,63 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       const int wr = shared ? d.R + m : seg_row(T, d.S, m);
       rowp = p.a + (int64_t)wr * (GEMM1 ? d.H : d.hstride);
     }
-    asrc[i] = rowp + (q & 7) * 16;
-    adst[i] = r * kStride + (q & 7) * 16;
-  }
-  if (tid < BM) {
-    const int m = min(m0 + tid, M - 1);
-    if (GEMM1 && shared) {
-      const int s = m / d.T_s, tt = m - s * d.T_s;
-      tscp = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
-    } else {
-      const int wr = shared ? d.R + m : seg_row(T, d.S, m);
-      tscp = p.as + (int64_t)wr * ((GEMM1 ? d.H : d.hstride) >> 7);
-    }
+    asrc[i] = rowp + c * 16;
   }
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
   const float* WS = static_cast<const float*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
-  // weight slab pieces: row-major rows, or the same bytes in the packed streaming order
-  // (pack_layout.h), where slab kb of a row block is one 8 KB run per wave
+  // weight slab pieces.  Packed (pack_layout.h): slab kb of the tile is four 8 KB runs,
+  // run v = the rows of tiled wave v (GEMM1: gate rows nb*128 + 32v + 0/16 and the
+  // matching up rows; GEMM2: rows nb*256 + 64v + 16 mt), each already in MFMA operand
+  // order [tile mt][half h][lane][16 B].  They are copied as they are, 1 KB per
+  // instruction, and read back at (run, mt, h, lane).  Row-major: rows in the swizzled
+  // layout of the tokens.  (Packed rows past a ragged end of H are the layout's
+  // padding: read, never stored.)
   const uint8_t* wsrc[kWLd];
-  int wdst[kWLd];
   const int64_t wstep = t_packed ? 8192 : 128;
 #pragma unroll
   for (int i = 0; i < kWLd; ++i) {
-    const int q = tid + kThreads * i;
+    const int q = (wave * kWLd + i) * 64 + lane;
     const int r = q >> 3;  // 0..255
+    const int c = (q & 7) ^ ((r >> 1) & 7);
     if (t_packed) {
-      int wv, mt, rr;
-      if (GEMM1) {
-        const int ro = r & 127;
-        wv = ro >> 5;
-        mt = (r >= 128 ? 2 : 0) + ((ro >> 4) & 1);
-        rr = ro & 15;
-      } else {
-        const int rc = min(r, d.H - 1 - nb * BN);
-        wv = rc >> 6;
-        mt = (rc >> 4) & 3;
-        rr = rc & 15;
-      }
-      const int h = (q & 7) >> 2, gq = q & 3;
-      wsrc[i] = W + pack_w_offset(MOE_FP8_E4M3, K, nb, wv, 0) + (mt * 2 + h) * 1024 + (gq * 16 + rr) * 16;
+      const int bi = wave * kWLd + i;  // 1 KB block bi of the slab: block bi % 8 of run bi / 8
+      wsrc[i] = W + pack_w_offset(MOE_FP8_E4M3, K, nb, bi >> 3, 0) + (bi & 7) * 1024 + lane * 16;
     } else {
       int wrow;
       if (GEMM1)
         wrow = (r < 128 ? 0 : inter) + nb * 128 + (r & 127);
       else
         wrow = min(nb * BN + r, d.H - 1);
-      wsrc[i] = W + (int64_t)wrow * K + (q & 7) * 16;
+      wsrc[i] = W + (int64_t)wrow * K + c * 16;
     }
-    wdst[i] = r * kStride + (q & 7) * 16;
   }
-  // weight scale rows of the tile's two 128-row blocks
+  // scales, one 4-byte DMA per wave per slab (so every wave issues the same number of
+  // loads per slab): waves 0-1 the token scales of rows 64 w + lane, wave 2 in lanes
+  // 0-1 the weight scales of the tile's two 128-row blocks, the rest into sdummy
   const float* ws0 = WS + (int64_t)(GEMM1 ? nb : min(2 * nb, (d.H >> 7) - 1)) * KB;
   const float* ws1 = WS + (int64_t)(GEMM1 ? (inter >> 7) + nb : min(2 * nb + 1, (d.H >> 7) - 1)) * KB;
+  const float* ssrc;
+  if (wave < 2) {
+    const int m = min(m0 + 64 * wave + lane, M - 1);
+    if (GEMM1 && shared) {
+      const int s = m / d.T_s, tt = m - s * d.T_s;
+      ssrc = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
+    } else {
+      const int wr = shared ? d.R + m : seg_row(T, d.S, m);
+      ssrc = p.as + (int64_t)wr * ((GEMM1 ? d.H : d.hstride) >> 7);
+    }
+  } else {
+    ssrc = lane == 1 ? ws1 : ws0;
+  }
 
-  u32x4 ra[kALd], rw[kWLd];
-  float rsx = 0.f, rsw = 0.f;
-  auto gload = [&](int kb) {
+  static_assert(kALd + kWLd + 1 == 7, "wait7_barrier() assumes 7 loads per slab and wave");
+  auto issue = [&](int kb, int st) {
 #pragma unroll
-    for (int i = 0; i < kALd; ++i) ra[i] = gload16(asrc[i] + (int64_t)kb * 128);
+    for (int i = 0; i < kALd; ++i) dma16(asrc[i] + (int64_t)kb * 128, &T.a[st][(wave * kALd + i) * 1024]);
 #pragma unroll
-    for (int i = 0; i < kWLd; ++i) rw[i] = gload16(wsrc[i] + (int64_t)kb * wstep);
-    if (tid < BM) rsx = gloadf(tscp + kb);
-    if (tid >= BM && tid < BM + 2) rsw = gloadf((tid == BM ? ws0 : ws1) + kb);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kALd; ++i) *reinterpret_cast<u32x4*>(&T.a[buf][adst[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kWLd; ++i) *reinterpret_cast<u32x4*>(&T.w[buf][wdst[i]]) = rw[i];
-    if (tid < BM) T.sx[buf][tid] = rsx;
-    if (tid >= BM && tid < BM + 2) T.sw[buf][tid - BM] = rsw;
+    for (int i = 0; i < kWLd; ++i) dma16(wsrc[i] + (int64_t)kb * wstep, &T.w[st][(wave * kWLd + i) * 1024]);
+    float* sdst = wave < 2 ? &T.sx[st][64 * wave] : (wave == 2 ? &T.sw[st][0] : &T.sdummy[0]);
+    dma4(ssrc + kb, sdst);
   };
 
   // this wave: token tiles wm*64 + 16*tt (tt = 0..3); weight tiles (GEMM1) gate rows
@@ -222,6 +257,16 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
   for (int j = 0; j < 4; ++j)
     wrows[j] = GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
   const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
+  // byte offsets (within a stage) of this lane's fragments
+  int woff[8], aoff[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    woff[2 * j] = t_packed ? wn * 8192 + (2 * j) * 1024 + lane * 16 : swz(wrows[j] + r16, g4);
+    woff[2 * j + 1] = t_packed ? wn * 8192 + (2 * j + 1) * 1024 + lane * 16 : swz(wrows[j] + r16, g4 + 4);
+    const int trow = wm * 64 + 16 * j + r16;
+    aoff[2 * j] = swz(trow, g4);
+    aoff[2 * j + 1] = swz(trow, g4 + 4);
+  }
 
   v4f acc[4][4];
 #pragma unroll
@@ -229,44 +274,43 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  __syncthreads();  // the previous item's last reads of the ring are done
+  issue(0, 0);
+  if (KB > 1) issue(1, 1);
   for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) gload(kb + 1);
-    v8i wv[4];
+    const int st = kb % kStages;
+    // this wave's loads of slab kb have landed (those of slab kb + 1 may stay in flight),
+    // then every wave's; stage (kb + 2) % 3 was last read at kb - 1
+    if (kb + 1 < KB)
+      wait7_barrier();
+    else
+      wait0_barrier();
+    if (kb + 2 < KB) issue(kb + 2, (kb + 2) % kStages);
+    const uint8_t* ws_ = T.w[st];
+    const uint8_t* as_ = T.a[st];
+    u32x4 wf[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* ap = &T.w[buf][(wrows[j] + r16) * kStride + 16 * g4];
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(ap);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(ap + 64);
-      wv[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    }
-    float swj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) swj[j] = T.sw[buf][GEMM1 ? (j >> 1) : wsel];
+    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const u32x4*>(ws_ + woff[i]);
+    const float swj[2] = {T.sw[st][0], T.sw[st][1]};
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      const int trow = wm * 64 + 16 * tt + r16;
-      const uint8_t* bp = &T.a[buf][trow * kStride + 16 * g4];
-      const u32x4 y0 = *reinterpret_cast<const u32x4*>(bp);
-      const u32x4 y1 = *reinterpret_cast<const u32x4*>(bp + 64);
-      const v8i bv = {(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-      const float sx = T.sx[buf][trow];
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(as_ + aoff[2 * tt]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(as_ + aoff[2 * tt + 1]);
+      const v8i bv = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      const float sx = T.sx[st][wm * 64 + 16 * tt + r16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const v8i wv = {(int)wf[2 * j].x, (int)wf[2 * j].y, (int)wf[2 * j].z, (int)wf[2 * j].w,
+                        (int)wf[2 * j + 1].x, (int)wf[2 * j + 1].y, (int)wf[2 * j + 1].z, (int)wf[2 * j + 1].w};
         const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wv[j], bv, v4f{0.f, 0.f, 0.f, 0.f}, MFMA_FMT_FP8, MFMA_FMT_FP8, 0, E8M0_ONE, 0, E8M0_ONE);
-        const float sc = swj[j] * sx;
+            wv, bv, v4f{0.f, 0.f, 0.f, 0.f}, MFMA_FMT_FP8, MFMA_FMT_FP8, 0, E8M0_ONE, 0, E8M0_ONE);
+        const float sc = swj[GEMM1 ? (j >> 1) : wsel] * sx;
         acc[j][tt][0] = fmaf(r[0], sc, acc[j][tt][0]);
         acc[j][tt][1] = fmaf(r[1], sc, acc[j][tt][1]);
         acc[j][tt][2] = fmaf(r[2], sc, acc[j][tt][2]);
         acc[j][tt][3] = fmaf(r[3], sc, acc[j][tt][3]);
       }
     }
-    if (kb + 1 < KB) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue; lane holds weight rows wrows[j] + 4*g4 + i of token wm*64 + 16*tt + r16
@@ -325,7 +369,11 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
   }
 }
 
-// Persistent grid: items of one GEMM, handed out by an atomic counter.
+// Persistent grid: the items of one GEMM from the per-XCD queues.  Queue x holds
+// super-tiles x, x + 8, ...; its counter k names slot k % 32 of its (k / 32)-th one.
+// Workgroup b runs on XCD b % 8 (the GPU's round-robin placement; any other placement
+// only costs locality).  Slots past an expert's last token tile or column block are
+// empty.  A workgroup leaves when every queue is exhausted.
 template <bool GEMM1>
 __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
   __shared__ Tiles T;
@@ -333,19 +381,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
   const BatchDims& d = p.d;
   const int nG = d.E + (d.Ish ? 1 : 0);
   const int* start = t.plan + (GEMM1 ? kPlanG1 : kPlanG2);
-  const int total = t.plan[GEMM1 ? 0 : 1];
-  int* ctr = t.plan + kPlanCtr + (GEMM1 ? 0 : 1);
-  for (;;) {
-    if (threadIdx.x == 0) T.item = atomicAdd(ctr, 1);
+  const int n_sup = t.plan[GEMM1 ? 0 : 1];
+  int* ctr = t.plan + kPlanCtr + (GEMM1 ? 0 : kXcds);
+  int q = blockIdx.x % kXcds;
+  for (int left = kXcds; left > 0;) {
+    if (threadIdx.x == 0) T.item = atomicAdd(ctr + q, 1);
     __syncthreads();
-    const int i = T.item;
-    if (i >= total) break;  // uniform
+    const int k = T.item;
+    __syncthreads();  // T.item is rewritten by the next round
+    const int sup = q + kXcds * (k / kSlots), slot = k % kSlots;
+    if (sup >= n_sup) {  // this queue is exhausted (uniform): move on to the next
+      q = (q + 1) % kXcds;
+      --left;
+      continue;
+    }
     int g = 0;
-    while (g + 1 < nG && i >= start[g + 1]) ++g;
+    while (g + 1 < nG && sup >= start[g + 1]) ++g;
     const int nbg = GEMM1 ? (g < d.E ? t.nb1_r : t.nb1_s) : t.nb2;
-    const int j = i - start[g];
-    const int tm = j / nbg, nb = j - tm * nbg;
+    const int ncb = (nbg + kSTN - 1) / kSTN;  // column super-blocks of g
+    const int j = sup - start[g];
+    const int tm = (j / ncb) * kSTM + slot / kSTN, nb = (j % ncb) * kSTN + slot % kSTN;
     const int M = t.plan[kPlanRows + g];
+    if (tm * BM >= M || nb >= nbg) continue;  // an empty slot (uniform)
     segments(p, g, T);
     __syncthreads();
     tile_item<GEMM1>(p, g, M, tm * BM, nb, T, t.packed != 0);
@@ -365,4 +422,4 @@ hipError_t launch_tiled(const TiledArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-int tiled_plan_words() { return kPlanCtr + 2; }
+int tiled_plan_words() { return kPlanCtr + 2 * kXcds; }
