@@ -7,19 +7,19 @@
 //
 // With hundreds to thousands of rows per expert the layer is bound by MFMA, not by the
 // weight stream, so both operands are reused from LDS: a workgroup computes a tile of
-// 128 token rows x 256 weight rows; per 128-deep K slab it stages the token slab
-// (16 KB), the weight slab (32 KB) and their scales in LDS, and each of its 8 waves
-// multiplies 64 tokens x 64 weight rows (16 MFMAs per slab), promoting every MFMA
+// 256 token rows x 256 weight rows; per 128-deep K slab it stages the token slab
+// (32 KB), the weight slab (32 KB) and their scales in LDS, and each of its 8 waves
+// multiplies 128 tokens x 64 weight rows (32 MFMAs per slab), promoting every MFMA
 // result with (weight scale x token scale).  The slabs go from memory straight into
-// a ring of three LDS stages (global_load_lds), two slabs ahead of the one being
-// multiplied, with no staging registers; one barrier per slab.  GEMM1's 256 weight rows are 128 gate + the matching
-// 128 up rows, so SwiGLU and the per-128-column requantisation stay in the epilogue.
+// a ring of two LDS stages (global_load_lds), the next slab in flight while one is
+// multiplied, with no staging registers; one barrier per slab.  GEMM1's 256 weight
+// rows are 128 gate + the matching 128 up rows, so SwiGLU and the per-128-column
+// requantisation stay in the epilogue.
 //
-// Work items are (expert, 128-row token tile, column block), grouped into super-tiles
+// Work items are (expert, 256-row token tile, column block), grouped into super-tiles
 // of 4 token tiles x 8 column blocks of one expert, built on the device from the row
 // counts (k_plan).  An XCD's 32 CUs work on one super-tile at a time, so its token
-// tiles and weight blocks are read once into that XCD's L2 and reused 8 and 4 times
-// (a 4.8x cut in L2 fill traffic against items spread over all XCDs).  Each XCD has
+// tiles and weight blocks are read once into that XCD's L2 and reused 8 and 4 times.  Each XCD has
 // its own queue of super-tiles (every 8th one), served by an atomic counter to a
 // persistent grid; when its queue is empty, a workgroup takes items from the next
 // XCD's queue, so skewed expert loads still balance across the GPU.
@@ -31,14 +31,18 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define GLOBAL __attribute__((address_space(1)))
 
-constexpr int BM = 128;            // token rows per tile
+constexpr int BM = 256;            // token rows per tile
 constexpr int BN = 256;            // weight rows per tile
 constexpr int kThreads = 512;      // 8 waves: 2 (token halves) x 4 (weight quarters)
+constexpr int kTT = BM / 32;       // 16-row token tiles per wave (each wave: BM/2 tokens x 64 weights)
 constexpr int kStride = 128;       // LDS bytes per staged 128-byte row (16-byte chunks swizzled)
 constexpr int kAPieces = BM * 8;   // 16-byte pieces of a token slab
 constexpr int kWPieces = BN * 8;   // 16-byte pieces of a weight slab
-constexpr int kALd = kAPieces / kThreads;  // 2
-constexpr int kWLd = kWPieces / kThreads;  // 4
+constexpr int kALd = kAPieces / kThreads;  // 16-byte token pieces per thread per slab
+constexpr int kWLd = kWPieces / kThreads;  // 16-byte weight pieces per thread per slab
+constexpr int kSxWaves = BM / 64;          // waves that load the token scales
+constexpr int kLoadsPerSlab = kALd + kWLd + 1;
+static_assert(kSxWaves < kThreads / 64, "a wave is left for the weight scales");
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const GLOBAL u32x4*)p; }
 __device__ __forceinline__ float gloadf(const float* p) { return *(const GLOBAL float*)p; }
@@ -68,16 +72,18 @@ __device__ __forceinline__ void dma4(const void* src, const void* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
-// Wait until at most 7 (or 0) of this wave's memory loads are in flight, then the
-// workgroup barrier, in one block: __syncthreads() would also wait for every pending
+// Wait until at most N of this wave's memory loads are in flight, then the workgroup
+// barrier, in one block: __syncthreads() would also wait for every pending
 // memory-to-LDS load, and a bare barrier intrinsic would let the compiler move memory
 // operations across it.  The memory clobber keeps both orders.
-__device__ __forceinline__ void wait7_barrier() { asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait0_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 
 
-constexpr int kStages = 3;  // LDS ring depth
+constexpr int kStages = 2;  // LDS ring depth: loads run kStages - 1 slabs ahead
 
 struct __align__(16) Tiles {
   uint8_t a[kStages][BM * kStride];
@@ -222,12 +228,13 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     }
   }
   // scales, one 4-byte DMA per wave per slab (so every wave issues the same number of
-  // loads per slab): waves 0-1 the token scales of rows 64 w + lane, wave 2 in lanes
-  // 0-1 the weight scales of the tile's two 128-row blocks, the rest into sdummy
+  // loads per slab): waves w < kSxWaves the token scales of rows 64 w + lane, wave
+  // kSxWaves in lanes 0-1 the weight scales of the tile's two 128-row blocks, the rest
+  // into sdummy
   const float* ws0 = WS + (int64_t)(GEMM1 ? nb : min(2 * nb, (d.H >> 7) - 1)) * KB;
   const float* ws1 = WS + (int64_t)(GEMM1 ? (inter >> 7) + nb : min(2 * nb + 1, (d.H >> 7) - 1)) * KB;
   const float* ssrc;
-  if (wave < 2) {
+  if (wave < kSxWaves) {
     const int m = min(m0 + 64 * wave + lane, M - 1);
     if (GEMM1 && shared) {
       const int s = m / d.T_s, tt = m - s * d.T_s;
@@ -240,17 +247,16 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     ssrc = lane == 1 ? ws1 : ws0;
   }
 
-  static_assert(kALd + kWLd + 1 == 7, "wait7_barrier() assumes 7 loads per slab and wave");
   auto issue = [&](int kb, int st) {
 #pragma unroll
     for (int i = 0; i < kALd; ++i) dma16(asrc[i] + (int64_t)kb * 128, &T.a[st][(wave * kALd + i) * 1024]);
 #pragma unroll
     for (int i = 0; i < kWLd; ++i) dma16(wsrc[i] + (int64_t)kb * wstep, &T.w[st][(wave * kWLd + i) * 1024]);
-    float* sdst = wave < 2 ? &T.sx[st][64 * wave] : (wave == 2 ? &T.sw[st][0] : &T.sdummy[0]);
+    float* sdst = wave < kSxWaves ? &T.sx[st][64 * wave] : (wave == kSxWaves ? &T.sw[st][0] : &T.sdummy[0]);
     dma4(ssrc + kb, sdst);
   };
 
-  // this wave: token tiles wm*64 + 16*tt (tt = 0..3); weight tiles (GEMM1) gate rows
+  // this wave: token tiles wm*(BM/2) + 16*tt (tt < kTT); weight tiles (GEMM1) gate rows
   // wn*32 + 16*j and up rows 128 + wn*32 + 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j
   int wrows[4];
 #pragma unroll
@@ -258,46 +264,49 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     wrows[j] = GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
   const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
   // byte offsets (within a stage) of this lane's fragments
-  int woff[8], aoff[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    woff[2 * j] = t_packed ? wn * 8192 + (2 * j) * 1024 + lane * 16 : swz(wrows[j] + r16, g4);
-    woff[2 * j + 1] = t_packed ? wn * 8192 + (2 * j + 1) * 1024 + lane * 16 : swz(wrows[j] + r16, g4 + 4);
-    const int trow = wm * 64 + 16 * j + r16;
-    aoff[2 * j] = swz(trow, g4);
-    aoff[2 * j + 1] = swz(trow, g4 + 4);
-  }
+  // Fragment offsets: tiles lie 16 or 128 rows apart, which leaves the swizzle term
+  // (r >> 1) & 7 unchanged, so every fragment is a base (two registers per operand)
+  // plus a constant the LDS instructions take as an immediate.
+  const int w0 = t_packed ? wn * 8192 + lane * 16 : swz(wrows[0] + r16, g4);
+  const int w1 = t_packed ? w0 + 1024 : swz(wrows[0] + r16, g4 + 4);
+  const int a0 = swz(wm * (BM / 2) + r16, g4), a1 = swz(wm * (BM / 2) + r16, g4 + 4);
+  auto wfrag_off = [&](int j, int h) {  // weight tile j, half h
+    const int base = h ? w1 : w0;
+    return t_packed ? base + 2 * j * 1024 : base + (wrows[j] - wrows[0]) * kStride;
+  };
 
-  v4f acc[4][4];
+  v4f acc[4][kTT];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < kTT; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int D = kStages - 1;  // slabs in flight ahead of the one multiplied
   __syncthreads();  // the previous item's last reads of the ring are done
-  issue(0, 0);
-  if (KB > 1) issue(1, 1);
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < KB) issue(i, i);
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb % kStages;
-    // this wave's loads of slab kb have landed (those of slab kb + 1 may stay in flight),
-    // then every wave's; stage (kb + 2) % 3 was last read at kb - 1
-    if (kb + 1 < KB)
-      wait7_barrier();
+    // this wave's loads of slab kb have landed (those of the D - 1 later slabs may stay
+    // in flight), then every wave's; stage (kb + D) % kStages was last read at kb - 1
+    if (D > 1 && kb + D - 1 < KB)
+      wait_barrier<(D > 1 ? D - 1 : 0) * kLoadsPerSlab>();
     else
-      wait0_barrier();
-    if (kb + 2 < KB) issue(kb + 2, (kb + 2) % kStages);
+      wait_barrier<0>();
+    if (kb + D < KB) issue(kb + D, (kb + D) % kStages);
     const uint8_t* ws_ = T.w[st];
     const uint8_t* as_ = T.a[st];
     u32x4 wf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const u32x4*>(ws_ + woff[i]);
+    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
     const float swj[2] = {T.sw[st][0], T.sw[st][1]};
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(as_ + aoff[2 * tt]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(as_ + aoff[2 * tt + 1]);
-      const v8i bv = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      const float sx = T.sx[st][wm * 64 + 16 * tt + r16];
+    for (int tt = 0; tt < kTT; ++tt) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(as_ + a0 + tt * 16 * kStride);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(as_ + a1 + tt * 16 * kStride);
+      const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      const float sx = T.sx[st][wm * (BM / 2) + 16 * tt + r16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v8i wv = {(int)wf[2 * j].x, (int)wf[2 * j].y, (int)wf[2 * j].z, (int)wf[2 * j].w,
@@ -313,29 +322,29 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     }
   }
 
-  // ---- epilogue; lane holds weight rows wrows[j] + 4*g4 + i of token wm*64 + 16*tt + r16
+  // ---- epilogue; lane holds weight rows wrows[j] + 4*g4 + i of token wm*(BM/2) + 16*tt + r16
   if constexpr (GEMM1) {
-    float hv[2][4][4];
+    // SwiGLU in place: acc[j] (gate, j = 0, 1) becomes h; acc[2 + j] (up) is then dead
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < kTT; ++tt) {
       float mx = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = silu(acc[j][tt][i]) * acc[2 + j][tt][i];
-          hv[j][tt][i] = v;
+          acc[j][tt][i] = v;
           mx = fmaxf(mx, fabsf(v));
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (g4 == 0) T.amax[wn][wm * 64 + 16 * tt + r16] = mx;
+      if (g4 == 0) T.amax[wn][wm * (BM / 2) + 16 * tt + r16] = mx;
     }
     __syncthreads();
     const int hsc_stride = d.hstride >> 7;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tr = wm * 64 + 16 * tt + r16;
+    for (int tt = 0; tt < kTT; ++tt) {
+      const int tr = wm * (BM / 2) + 16 * tt + r16;
       const int m = m0 + tr;
       if (m >= M) continue;
       const int orow = shared ? d.R + m : seg_row(T, d.S, m);
@@ -345,7 +354,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       for (int j = 0; j < 2; ++j) {
         float q[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(hv[j][tt][i] / sc, -448.0f), 448.0f);
+        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[j][tt][i] / sc, -448.0f), 448.0f);
         *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow * d.hstride + nb * 128 + wn * 32 + 16 * j + 4 * g4) =
             pack4_e4m3(q[0], q[1], q[2], q[3]);
       }
@@ -353,8 +362,8 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     }
   } else {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int m = m0 + wm * 64 + 16 * tt + r16;
+    for (int tt = 0; tt < kTT; ++tt) {
+      const int m = m0 + wm * (BM / 2) + 16 * tt + r16;
       if (m >= M) continue;
       const int orow = shared ? d.R + m : seg_row(T, d.S, m);
 #pragma unroll
