@@ -86,6 +86,8 @@ def load():
         "moe_set_timing": (st, [VP, I32]),
         "moe_set_option": (st, [VP, ctypes.c_int, I32]),
         "moe_read_timing": (st, [VP, P(ctypes.c_float), P(I32)]),
+        "moe_router_logits": (st, [I32, I32, I32, VP, VP, VP, VP]),
+        "moe_topk_softmax": (st, [I32, I32, I32, VP, VP, VP, VP]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
     }
@@ -113,6 +115,27 @@ def make_config(S, max_tokens, H, I, E, k, act="fp8", weight="fp8", out="bf16", 
                 sched=MOE_SCHED_FENCE, dispatch_cus=0):
     return MoeConfig(S, max_tokens, H, I, E, k, shared_I, _DTYPE[act], _DTYPE[weight], _DTYPE[out],
                      sched, dispatch_cus)
+
+
+def router_logits(x, wr, logits=None):
+    """logits [T][E] fp32 = x [T][H] bf16 . wr [E][H] bf16^T on the current stream."""
+    lib = load()
+    T, H = x.shape
+    E = wr.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib.moe_router_logits(T, H, E, _ptr(x), _ptr(wr), _ptr(logits), _stream()))
+    return logits
+
+
+def topk_softmax(logits, k):
+    """(ids [T][k] int32, w [T][k] fp32) from logits [T][E] fp32 on the current stream."""
+    lib = load()
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib.moe_topk_softmax(T, E, k, _ptr(logits), _ptr(ids), _ptr(w), _stream()))
+    return ids, w
 
 
 class DeviceInputs:

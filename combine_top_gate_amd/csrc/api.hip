@@ -674,6 +674,37 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);
 }
 
+moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const void* x, const void* wr, float* logits,
+                             hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  if (H <= 0 || H % 32) return fail(MOE_ERR_INVALID_ARG, "H %d is not a positive multiple of 32", H);
+  if (E < 1 || E > MOE_MAX_GATE_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "E %d outside 1..%d", E, MOE_MAX_GATE_EXPERTS);
+  if (T == 0) return MOE_OK;
+  if (!x || !wr || !logits) return fail(MOE_ERR_INVALID_ARG, "x, wr or logits is NULL");
+  if (!aligned16(x) || !aligned16(wr) || ((uintptr_t)logits & 3u))
+    return fail(MOE_ERR_INVALID_ARG, "x and wr must be 16-byte aligned, logits 4-byte aligned");
+  RouterArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), logits, T, H, E};
+  HIP_TRY(launch_router(a, stream));
+  return MOE_OK;
+}
+
+moe_status moe_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits, int32_t* ids, float* w,
+                            hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  if (E < 1 || E > MOE_MAX_GATE_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "E %d outside 1..%d", E, MOE_MAX_GATE_EXPERTS);
+  if (k < 1 || k > MOE_MAX_TOPK || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "k %d outside 1..min(%d, E)", k, MOE_MAX_TOPK);
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "logits, ids or w is NULL");
+  if (((uintptr_t)logits | (uintptr_t)ids | (uintptr_t)w) & 3u)
+    return fail(MOE_ERR_INVALID_ARG, "logits, ids and w must be 4-byte aligned");
+  TopkArgs a{logits, ids, w, T, E, k};
+  HIP_TRY(launch_topk(a, stream));
+  return MOE_OK;
+}
+
 moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {
   if (!c || !bits) return fail(MOE_ERR_INVALID_ARG, "ctx or bits is NULL");
   HIP_TRY(hipDeviceSynchronize());

@@ -63,14 +63,26 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(u
 // of them it would wait for every one in flight (later stages included) before any
 // LDS read.  It does not need to know: the data is read only after wait7_barrier() /
 // wait0_barrier(), whose memory clobbers also keep every LDS access on its side.
-// No register is written, so nothing of the load is left to land in a register.
+// No register is written, so nothing of the load is left to land in a register.  M0
+// (the LDS base, read when the load issues) is saved and restored around it, with the
+// wait state an LDS-DMA needs after an M0 write.
 __device__ __forceinline__ void dma16(const void* src, const void* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_off(dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
 }
 __device__ __forceinline__ void dma4(const void* src, const void* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_off(dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
 }
 // Wait until at most N of this wave's memory loads are in flight, then the workgroup
 // barrier, in one block: __syncthreads() would also wait for every pending

@@ -122,3 +122,20 @@ struct CombineArgs {
   int out_f32;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// ---- gating (ahead of dispatch) ----------------------------------------------
+struct RouterArgs {
+  const uint16_t* x;   // [T][H] bf16
+  const uint16_t* wr;  // [E][H] bf16
+  float* logits;       // [T][E]
+  int T, H, E;         // H a multiple of 32
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+
+struct TopkArgs {
+  const float* logits;  // [T][E], E <= 256
+  int32_t* ids;         // [T][k]
+  float* w;             // [T][k]
+  int T, E, k;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);

@@ -248,3 +248,32 @@ def make_inputs(name="decode128_fp8", **over):
         inp.sh_w2, inp.sh_s2 = c[0], (d[0] if d is not None else None)
     inp.extra = cfg
     return inp
+
+
+# ------------------------------------------------------------ gating inputs
+@dataclass
+class RouterInputs:
+    """Hidden states and router weights for the gate, as bf16 bit patterns."""
+    x_bits: np.ndarray   # uint16 [T][H]
+    wr_bits: np.ndarray  # uint16 [E][H]
+    T: int
+    H: int
+    E: int
+
+
+def _bf16_bits(a):
+    """Round to bf16 with torch's cast and return the 16-bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().astype(np.uint16)
+
+
+def make_router_inputs(T, H, E, seed=0):
+    """x ~ N(0, 1) [T][H] and wr ~ N(0, 1/H) [E][H] (logits of unit scale), in bf16.
+
+    The router of a DeepSeek-V3-shaped layer scores all 256 global experts; streams:
+    SeedSequence(seed).spawn(2) -> x, wr."""
+    sx, sw = np.random.SeedSequence(seed).spawn(2)
+    x = np.random.Generator(np.random.PCG64(sx)).standard_normal((T, H))
+    wr = np.random.Generator(np.random.PCG64(sw)).standard_normal((E, H)) / np.sqrt(H)
+    return RouterInputs(_bf16_bits(x), _bf16_bits(wr), T, H, E)
+

@@ -251,6 +251,32 @@ typedef enum {
 } moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 
+/*
+ * Gating ahead of dispatch.  Each token goes to the experts its gating result names
+ * ["GC-MoE: Decoupling MoE Communication and Computation with CUDA Green Contexts",
+ * "Why Expert Parallelism Is Inefficient in MoE Decoding"]; the gate is the
+ * sparsely-gated MoE layer's ["Relay Buffer Independent Communication over Pooled HBM
+ * for Efficient MoE Inference on Ascend", "Builds on"]: the k largest logits of a
+ * token (ties to the lower expert id; slot 0 holds the largest), weights = softmax
+ * over the kept logits.  Neither call needs a context; neither allocates.
+ *
+ * moe_router_logits: logits[t][e] = sum_h x[t][h] * wr[e][h] for T tokens and E
+ *   experts; x [T][H] and wr [E][H] bf16 (16-byte aligned), H a multiple of 32,
+ *   E <= MOE_MAX_GATE_EXPERTS; logits [T][E] fp32 (caller-owned).  fp32 accumulation
+ *   (MFMA); the order of the sum is the kernel's.
+ * moe_topk_softmax: from logits [T][E] fp32 to ids [T][k] int32 (descending logit)
+ *   and w [T][k] fp32 (sums to 1 per token); k <= min(E, MOE_MAX_TOPK).  The
+ *   selection compares the given fp32 values exactly, so it is reproducible: the
+ *   same logits always give the same ids.
+ * T = 0 is a no-op.  Invalid sizes or pointers return MOE_ERR_INVALID_ARG before any
+ * work is enqueued.
+ */
+#define MOE_MAX_GATE_EXPERTS 256
+moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const void* x, const void* wr, float* logits,
+                             hipStream_t stream);
+moe_status moe_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits, int32_t* ids, float* w,
+                            hipStream_t stream);
+
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 

@@ -128,6 +128,12 @@ def bf16_round(x):
     return np.ldexp(r, e - 8)
 
 
+def bf16_decode(bits):
+    """bf16 bit patterns (uint16) -> fp64 values: the top 16 bits of an IEEE fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
 def fp32_round(x):
     """Round fp64 values to the nearest fp32 value (IEEE round to nearest even)."""
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)

@@ -36,3 +36,14 @@ def softmax_topk(logits, k):
             ids[t, j] = e
             w[t, j] = ex[j] / tot
     return ids, w
+
+
+def router_logits(x, wr):
+    """Router scores: logits[t][e] = sum_h x[t][h] * wr[e][h], in fp64.
+
+    x [T][H] and wr [E][H] are the values of the bf16 inputs (codecs.bf16_decode).
+    The pages name the gating result, not the router; this is the plain linear
+    router of the sparsely-gated MoE layer the relay-free Ascend page builds on.
+    """
+    return np.asarray(x, dtype=np.float64) @ np.asarray(wr, dtype=np.float64).T
+

@@ -73,3 +73,44 @@ def test_valid_config_without_device_is_hip_error(lib):
     cfg = binding.make_config(2, 4, 256, 128, 4, 2)
     st, ctx, msg = _create(lib, cfg)
     assert st == binding.MOE_ERR_HIP and not ctx.value
+
+
+# Fake, never-dereferenced device addresses: every case below must be refused on
+# the host before anything reaches the device.
+_A16 = ctypes.c_void_p(0x10000)
+_A4 = ctypes.c_void_p(0x10004)
+
+
+@pytest.mark.parametrize("T,H,E,x,wr,lg,needle", [
+    (-1, 256, 8, _A16, _A16, _A16, "T"),
+    (4, 100, 8, _A16, _A16, _A16, "H"),
+    (4, 0, 8, _A16, _A16, _A16, "H"),
+    (4, 256, 0, _A16, _A16, _A16, "E"),
+    (4, 256, 257, _A16, _A16, _A16, "E"),
+    (4, 256, 8, None, _A16, _A16, "NULL"),
+    (4, 256, 8, _A4, _A16, _A16, "aligned"),
+    (4, 256, 8, _A16, _A16, ctypes.c_void_p(0x10002), "aligned"),
+])
+def test_router_logits_rejects_bad_arguments(lib, T, H, E, x, wr, lg, needle):
+    assert lib.moe_router_logits(T, H, E, x, wr, lg, None) == binding.MOE_ERR_INVALID_ARG
+    assert needle in lib.moe_last_error_message().decode()
+
+
+@pytest.mark.parametrize("T,E,k,lg,ids,w,needle", [
+    (-1, 8, 2, _A16, _A16, _A16, "T"),
+    (4, 0, 1, _A16, _A16, _A16, "E"),
+    (4, 300, 8, _A16, _A16, _A16, "E"),
+    (4, 8, 0, _A16, _A16, _A16, "k"),
+    (4, 8, 9, _A16, _A16, _A16, "k"),
+    (4, 64, 17, _A16, _A16, _A16, "k"),
+    (4, 8, 2, _A16, None, _A16, "NULL"),
+    (4, 8, 2, _A16, _A16, ctypes.c_void_p(0x10001), "aligned"),
+])
+def test_topk_softmax_rejects_bad_arguments(lib, T, E, k, lg, ids, w, needle):
+    assert lib.moe_topk_softmax(T, E, k, lg, ids, w, None) == binding.MOE_ERR_INVALID_ARG
+    assert needle in lib.moe_last_error_message().decode()
+
+
+def test_gate_calls_with_no_tokens_are_no_ops(lib):
+    assert lib.moe_router_logits(0, 256, 8, None, None, None, None) == binding.MOE_OK
+    assert lib.moe_topk_softmax(0, 8, 2, None, None, None, None) == binding.MOE_OK

@@ -1,0 +1,130 @@
+"""GPU parity of the gate ahead of dispatch (router logits, then top-k softmax)
+through the C-ABI, against the oracle's router_logits and softmax_topk.
+
+Bars:
+  top-k ids   bit-exact when both sides see the same fp32 logits: the selection is
+              a comparison of fp32 values, and fp32 -> fp64 keeps their order.
+  top-k w     |g - r| <= (2 * spread + k + 6) * 2^-24 * r + 2^-40 per weight, with
+              spread = max |z_j - z_max| over the token's finite kept logits (a
+              -inf logit's weight is 0 on both sides): the kernel
+              forms z_j - z_max in fp32 (relative error <= u * spread carried into
+              exp), expf (a few ulp), a k-term fp32 sum and one division.
+  logits      |g - r| <= gamma_n * sum_h |x_h * w_h| + 2^-60, n = 32 + H / 128 + 4:
+              bf16 x bf16 products are exact in fp32; a 32-deep MFMA step is
+              counted as 32 sequential fp32 additions, each of the 4 waves chains
+              H / 128 steps, and 4 partial sums are added (Higham, gamma_n = n u /
+              (1 - n u), u = 2^-24).
+  end to end  ids equal the oracle's wherever the gap between the k-th and the
+              (k+1)-th fp64 logit exceeds twice the logits bound; everywhere, the
+              ids are the exact top-k of the GPU's own logits.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_top_gate_amd import binding, synth
+from oracle import codecs, gating
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def dev_bits(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def check_topk(z32, k):
+    """Run the kernel on fp32 logits z32 [T][E]; compare ids exactly and weights to the bound."""
+    zd = torch.from_numpy(np.ascontiguousarray(z32, dtype=np.float32)).cuda()
+    ids, w = binding.topk_softmax(zd, k)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    rid, rw = gating.softmax_topk(z32.astype(np.float64), k)
+    assert np.array_equal(ids, rid)
+    sel = np.take_along_axis(z32.astype(np.float64), rid.astype(np.int64), axis=1)
+    # -inf logits get weight exactly 0 on both sides; the spread is over the finite ones
+    spread = np.max(np.where(np.isfinite(sel), sel[:, :1] - sel, 0.0), axis=1, keepdims=True)
+    bound = (2 * spread + k + 6) * U * rw + 2.0 ** -40
+    assert np.all(np.abs(w - rw) <= bound), float(np.max(np.abs(w - rw) / bound))
+    return ids
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 8, 2), (37, 40, 8), (130, 200, 8),
+                                   (64, 256, 16), (300, 256, 8), (3, 64, 1)])
+def test_topk_softmax_matches_oracle(lib, T, E, k):
+    rng = np.random.default_rng(1000 + T + E + k)
+    z = synth.draw_logits(rng, T, E, "normal").astype(np.float32)
+    check_topk(z, k)
+
+
+def test_topk_softmax_ties_and_infinities(lib):
+    rng = np.random.default_rng(7)
+    # values on a coarse grid: many exact ties, broken to the lower expert id
+    z = (np.round(rng.standard_normal((96, 256)) * 2) / 4).astype(np.float32)
+    z[0, :] = 1.0                      # all equal: ids 0..k-1 in order, equal weights
+    z[1, :] = -np.inf                  # all -inf except two
+    z[1, 17] = 0.0
+    z[1, 200] = 0.0
+    z[2, 100:] = -np.inf
+    ids = check_topk(z, 8)
+    assert list(ids[0]) == list(range(8))
+    assert list(ids[1][:2]) == [17, 200]
+
+
+def test_topk_softmax_zipf_routing(lib):
+    rng = np.random.default_rng(11)
+    z = synth.draw_logits(rng, 512, 256, "zipf").astype(np.float32)
+    check_topk(z, 8)
+
+
+def router_case(T, H, E, seed):
+    ri = synth.make_router_inputs(T, H, E, seed=seed)
+    g = binding.router_logits(dev_bits(ri.x_bits), dev_bits(ri.wr_bits))
+    torch.cuda.synchronize()
+    g = g.cpu().numpy().astype(np.float64)
+    x, wr = codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits)
+    r = gating.router_logits(x, wr)
+    mag = gating.router_logits(np.abs(x), np.abs(wr))
+    bound = gamma(32 + H // 128 + 4) * mag + 2.0 ** -60
+    return g, r, bound
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 32, 1), (5, 64, 7), (17, 96, 33), (40, 512, 64),
+                                   (33, 1056, 250), (130, 2048, 256)])
+def test_router_logits_within_fp32_bound(lib, T, H, E):
+    g, r, bound = router_case(T, H, E, seed=T * 131 + E)
+    err = np.abs(g - r)
+    print(f"  T {T} H {H} E {E}: max err/bound {np.max(err / bound):.3f}", flush=True)
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("T", [128, 1024])
+def test_gate_full_size_end_to_end(lib, T):
+    """DeepSeek-V3-shaped gate: H 7168, 256 experts, top-8, one decode batch (128
+    tokens) and all eight sources' batches at once (1024)."""
+    H, E, k = 7168, 256, 8
+    g, r, bound = router_case(T, H, E, seed=T)
+    assert np.all(np.abs(g - r) <= bound)
+    ids = check_topk(g.astype(np.float32), k)
+    rs = -np.sort(-r, axis=1)
+    margin = rs[:, k - 1] - rs[:, k]
+    clear = margin > 2 * bound.max(axis=1)
+    rid, _ = gating.softmax_topk(r, k)
+    print(f"  T {T}: {int(clear.sum())} of {T} tokens with a clear top-{k} margin", flush=True)
+    assert clear.mean() > 0.9
+    assert np.array_equal(np.sort(ids[clear], axis=1), np.sort(rid[clear], axis=1))
+
+
+def test_gate_calls_after_empty_batch(lib):
+    zd = torch.zeros((0, 16), dtype=torch.float32, device="cuda")
+    ids, w = binding.topk_softmax(zd, 4)
+    assert ids.shape == (0, 4)
+    lg = binding.router_logits(torch.zeros((0, 64), dtype=torch.int16, device="cuda"),
+                               torch.zeros((16, 64), dtype=torch.int16, device="cuda"))
+    assert lg.shape == (0, 16)
+    check_topk(np.arange(32, dtype=np.float32)[None, :].repeat(3, 0), 4)

@@ -1,8 +1,11 @@
 """Pins for the oracle's top-k softmax gate: torch.topk + torch.softmax (library
 routines), closed forms (k = 1 gives weight 1, weights sum to 1) and the tie rule."""
+import math
+
 import numpy as np
 import torch
 
+from oracle import codecs, gating
 from oracle.gating import softmax_topk
 from combine_top_gate_amd import synth
 
@@ -50,3 +53,34 @@ def test_zipf_routing_popularity_decreases():
     assert load[0] > load[8] > load[31] > 0
     # k distinct experts per token
     assert all(len(set(r)) == inp.k for r in inp.ids.reshape(-1, inp.k).tolist())
+
+
+def test_bf16_decode_matches_torch_on_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    got = codecs.bf16_decode(bits)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_router_logits_brute_force_and_one_hot():
+    rng = np.random.default_rng(5)
+    x = codecs.bf16_decode(synth._bf16_bits(rng.standard_normal((3, 5))))
+    wr = codecs.bf16_decode(synth._bf16_bits(rng.standard_normal((4, 5))))
+    got = gating.router_logits(x, wr)
+    for t in range(3):
+        for e in range(4):
+            want = math.fsum(float(x[t, h]) * float(wr[e, h]) for h in range(5))
+            assert abs(got[t, e] - want) <= 1e-15 * max(1.0, abs(want))
+    # a one-hot token row picks one column of the router weights, exactly
+    onehot = np.zeros((5, 5))
+    onehot[np.arange(5), np.arange(5)] = 1.0
+    assert np.array_equal(gating.router_logits(onehot, wr), wr.T)
+
+
+def test_router_inputs_are_deterministic_bf16():
+    a = synth.make_router_inputs(4, 64, 8, seed=3)
+    b = synth.make_router_inputs(4, 64, 8, seed=3)
+    assert np.array_equal(a.x_bits, b.x_bits) and np.array_equal(a.wr_bits, b.wr_bits)
+    wr = codecs.bf16_decode(a.wr_bits)
+    assert 0.05 < np.std(wr) * np.sqrt(64) < 5
