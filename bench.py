@@ -50,6 +50,8 @@ def parse():
                     help="synchronisation between dispatch and GEMM1")
     ap.add_argument("--dispatch-cus", type=int, default=0,
                     help="SENTINEL: CUs of the dispatch stream (multiple of 8; 0 = library default)")
+    ap.add_argument("--no-gate", action="store_true",
+                    help="skip the separate timing of the gate (router + top-k) ahead of dispatch")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -98,6 +100,37 @@ def read_traffic():
         return None
     sha = hashlib.sha256(open(GEMM1_SRC, "rb").read()).hexdigest()
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+GATE_EXPERTS = 256  # the router scores every global expert (DeepSeek-V3 shape)
+
+
+def time_gate(torch, binding, synth, T, H, k, calls=200):
+    """Microseconds per fused gate call (router + top-k softmax) for T tokens.
+
+    The calls are plain stream launches, as the layer's are.  A GPU-side spin is queued
+    first so that all the calls are enqueued before the first one starts: the events then
+    time the GPU's back-to-back work, not the host's call overhead."""
+    ri = synth.make_router_inputs(T, H, GATE_EXPERTS, seed=11)
+    x = torch.from_numpy(ri.x_bits.view("int16")).cuda()
+    wr = torch.from_numpy(ri.wr_bits.view("int16")).cuda()
+    ws = torch.empty(binding.gate_workspace_bytes(T, H, GATE_EXPERTS) // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        binding.gate(x, wr, k, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(50_000_000)
+    e0.record()
+    h0 = time.perf_counter()
+    for _ in range(calls):
+        binding.gate(x, wr, k, workspace=ws)
+    h1 = time.perf_counter()
+    e1.record()
+    torch.cuda.synchronize()
+    gpu_us = e0.elapsed_time(e1) * 1e3 / calls
+    return {"tokens": T, "hidden": H, "experts": GATE_EXPERTS, "topk": k, "us_per_call": round(gpu_us, 2),
+            "host_us_per_call": round((h1 - h0) * 1e6 / calls, 2),
+            "method": f"{calls} back-to-back calls queued behind a GPU spin, HIP events"}
 
 
 def cpu_baseline(inp, n_experts, repeats):
@@ -236,6 +269,9 @@ def main():
                      "frac": round(g1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes["gemm1"]},
     }
+    if not args.no_gate:
+        print("[bench] gate timing", file=sys.stderr, flush=True)
+        rec["gate_us"] = time_gate(torch, binding, synth, inp.S * inp.T_s, inp.H, inp.k)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_experts, args.cpu_repeats)

@@ -88,6 +88,8 @@ def load():
         "moe_read_timing": (st, [VP, P(ctypes.c_float), P(I32)]),
         "moe_router_logits": (st, [I32, I32, I32, VP, VP, VP, VP]),
         "moe_topk_softmax": (st, [I32, I32, I32, VP, VP, VP, VP]),
+        "moe_gate_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32]),
+        "moe_gate": (st, [I32, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP, VP, VP, VP]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
     }
@@ -126,6 +128,30 @@ def router_logits(x, wr, logits=None):
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _check(lib.moe_router_logits(T, H, E, _ptr(x), _ptr(wr), _ptr(logits), _stream()))
     return logits
+
+
+def gate(x, wr, k, workspace=None, want_logits=False):
+    """(ids, w[, logits]) for x [T][H] bf16 and wr [E][H] bf16 through the fused gate.
+
+    workspace: a device tensor of at least gate_workspace_bytes(T, H, E) bytes, or None to
+    allocate one here."""
+    lib = load()
+    T, H = x.shape
+    E = wr.shape[0]
+    need = lib.moe_gate_workspace_bytes(T, H, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.moe_gate(T, H, E, k, _ptr(x), _ptr(wr), _ptr(workspace), nbytes, _ptr(logits), _ptr(ids),
+                        _ptr(w), _stream()))
+    return (ids, w, logits) if want_logits else (ids, w)
+
+
+def gate_workspace_bytes(T, H, E):
+    return load().moe_gate_workspace_bytes(T, H, E)
 
 
 def topk_softmax(logits, k):

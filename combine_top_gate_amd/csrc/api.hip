@@ -700,8 +700,39 @@ moe_status moe_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits
   if (!logits || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "logits, ids or w is NULL");
   if (((uintptr_t)logits | (uintptr_t)ids | (uintptr_t)w) & 3u)
     return fail(MOE_ERR_INVALID_ARG, "logits, ids and w must be 4-byte aligned");
-  TopkArgs a{logits, ids, w, T, E, k};
+  TopkArgs a{logits, nullptr, ids, w, T, E, k, 1};
   HIP_TRY(launch_topk(a, stream));
+  return MOE_OK;
+}
+
+size_t moe_gate_workspace_bytes(int32_t T, int32_t H, int32_t E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return (size_t)gate_split(T, H, E) * (size_t)T * (size_t)E * sizeof(float);
+}
+
+moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, void* workspace,
+                    size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  if (H <= 0 || H % 32) return fail(MOE_ERR_INVALID_ARG, "H %d is not a positive multiple of 32", H);
+  if (E < 1 || E > MOE_MAX_GATE_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "E %d outside 1..%d", E, MOE_MAX_GATE_EXPERTS);
+  if (k < 1 || k > MOE_MAX_TOPK || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "k %d outside 1..min(%d, E)", k, MOE_MAX_TOPK);
+  if (T == 0) return MOE_OK;
+  if (!x || !wr || !workspace || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "x, wr, workspace, ids or w is NULL");
+  if (!aligned16(x) || !aligned16(wr) || !aligned16(workspace))
+    return fail(MOE_ERR_INVALID_ARG, "x, wr and workspace must be 16-byte aligned");
+  if (((uintptr_t)ids | (uintptr_t)w | (uintptr_t)logits) & 3u)
+    return fail(MOE_ERR_INVALID_ARG, "logits, ids and w must be 4-byte aligned");
+  const size_t need = moe_gate_workspace_bytes(T, H, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes; this shape needs %zu", workspace_bytes, need);
+  const int ks = gate_split(T, H, E);
+  float* part = static_cast<float*>(workspace);
+  RouterSplitArgs ra{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), part, T, H, E, ks};
+  HIP_TRY(launch_router_split(ra, stream));
+  TopkArgs ta{part, logits, ids, w, T, E, k, ks};
+  HIP_TRY(launch_topk(ta, stream));
   return MOE_OK;
 }
 

@@ -11,13 +11,26 @@
 // k_router: logits[t][e] = sum_h x[t][h] * wr[e][h], bf16 inputs, fp32 accumulation,
 // on v_mfma_f32_16x16x32_bf16 (measured on gfx950: lane l, element i of the A operand is
 // row l % 16 at k = 8 (l / 16) + i, the same for B's columns; result lane l, register i
-// is row 4 (l / 16) + i, column l % 16).  A workgroup owns 16 experts x 16 tokens; its 4
-// waves split H and add their partial tiles through LDS.  Experts sit in the A slot and
-// tokens in the B slot, so each lane's operands are 16 contiguous bytes of a row.
+// is row 4 (l / 16) + i, column l % 16).  A workgroup owns 16 experts x 16 TT tokens;
+// its waves split the H / 32 MFMA steps round-robin and issue a whole batch of steps'
+// loads before the first MFMA, so a wave waits on memory once per batch, not per step.
+// The partial tiles are added through LDS in wave order (a fixed order: the result does
+// not depend on timing).  Experts sit in the A slot and tokens in the B slot, so each
+// lane's operands are 16 contiguous bytes of a row.
 //
-// k_topk: one wave per token; E <= 256 logits, 4 per lane; k rounds of a wave argmax
-// ordered by (logit descending, expert id ascending), then the softmax in fp32.
+// k_router_split (the fused gate's first launch): the same tiles, with the K steps also
+// split into ks contiguous slices over workgroups, so that a small batch still spreads
+// over every CU; each workgroup writes its slice's partial tile to a workspace.
+//
+// k_topk: one wave per token, E <= 256 logits, 4 per lane (added up from the ks partial
+// sums in slice order first, when there are several).  The k-th largest logit is
+// found exactly by a radix select over order-preserving 32-bit keys (one ballot per
+// lane register and bit); the k selected logits (ties at the threshold to the lower
+// expert ids) go to LDS, where each is ranked by (logit descending, id ascending) and
+// the softmax over them is taken in fp32.
 #include <math.h>
+
+#include <algorithm>
 
 #include "kernels.h"
 
@@ -38,103 +51,245 @@ __device__ __forceinline__ v8s as_v8s(u32x4 v) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void k_router(RouterArgs a) {
-  __shared__ float s_part[4][64][4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+// TT token tiles per workgroup, W waves splitting K, NB steps in flight per wave.
+template <int TT, int W, int NB>
+__global__ __launch_bounds__(64 * W) void k_router(RouterArgs a) {
+  __shared__ v4f s_part[W][TT][64];
+  // the wave index is made a scalar so the step loop and its bounds test stay uniform
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int eb = blockIdx.x, tb = blockIdx.y;
+  if (TT > 1) {
+    // Workgroups reach the 8 XCDs round-robin by linear id.  Renumber them so that XCD x
+    // takes one contiguous run of token tiles with every expert block: a token tile is
+    // then fetched into one XCD's L2 once and read there by all expert blocks.
+    const int n = gridDim.x * gridDim.y, b = blockIdx.x + gridDim.x * blockIdx.y;
+    const int xcd = b & 7, per = n >> 3, extra = n & 7;
+    const int L = xcd * per + min(xcd, extra) + (b >> 3);
+    eb = L % gridDim.x;
+    tb = L / gridDim.x;
+  }
+  const int e0 = eb * 16, t0 = tb * 16 * TT;
   const int r16 = lane & 15, g4 = lane >> 4;
   // rows past the end repeat the last one (their results are not stored)
-  const int e = min(e0 + r16, a.E - 1), t = min(t0 + r16, a.T - 1);
-  const uint16_t* wrow = a.wr + (int64_t)e * a.H + 8 * g4;
-  const uint16_t* xrow = a.x + (int64_t)t * a.H + 8 * g4;
-  const int steps = a.H / 32;  // 32-deep K steps, split over the 4 waves
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  int s = wave;
-  for (; s + 12 < steps; s += 16) {  // four steps in flight per wave
-    u32x4 wa[4], xb[4];
+  const uint16_t* wrow = a.wr + (int64_t)min(e0 + r16, a.E - 1) * a.H + 8 * g4;
+  const uint16_t* xrow[TT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wa[u] = gload16(wrow + (int64_t)(s + 4 * u) * 32);
-      xb[u] = gload16(xrow + (int64_t)(s + 4 * u) * 32);
+  for (int u = 0; u < TT; ++u) xrow[u] = a.x + (int64_t)min(t0 + 16 * u + r16, a.T - 1) * a.H + 8 * g4;
+  const int steps = a.H / 32;
+  v4f acc[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  int s0 = wave;
+  for (; s0 + (NB - 1) * W < steps; s0 += W * NB) {  // whole batches: every load before any MFMA
+    u32x4 wa[NB], xb[NB][TT];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t off = (int64_t)(s0 + i * W) * 32;
+      wa[i] = gload16(wrow + off);
+#pragma unroll
+      for (int u = 0; u < TT; ++u) xb[i][u] = gload16(xrow[u] + off);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the MFMAs
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(wa[u]), as_v8s(xb[u]), acc, 0, 0, 0);
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(wa[i]), as_v8s(xb[i][u]), acc[u], 0, 0, 0);
   }
-  for (; s < steps; s += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(gload16(wrow + (int64_t)s * 32)),
-                                                   as_v8s(gload16(xrow + (int64_t)s * 32)), acc, 0, 0, 0);
+  for (; s0 < steps; s0 += W) {  // the rest, a step at a time
+    const int64_t off = (int64_t)s0 * 32;
+    const u32x4 wa = gload16(wrow + off);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_part[wave][lane][i] = acc[i];
+    for (int u = 0; u < TT; ++u)
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(wa), as_v8s(gload16(xrow[u] + off)), acc[u], 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < TT; ++u) s_part[wave][u][lane] = acc[u];
   __syncthreads();
-  if (wave == 0) {
+  for (int idx = threadIdx.x; idx < TT * 64 * 4; idx += 64 * W) {
+    const int u = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
+    float v = s_part[0][u][l][i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // the four waves' partial sums, added in wave order
-      const float v = ((s_part[0][lane][i] + s_part[1][lane][i]) + s_part[2][lane][i]) + s_part[3][lane][i];
-      const int er = e0 + 4 * g4 + i, tc = t0 + r16;  // result row = expert, column = token
-      if (er < a.E && tc < a.T) a.logits[(int64_t)tc * a.E + er] = v;
-    }
+    for (int w = 1; w < W; ++w) v += s_part[w][u][l][i];
+    const int er = e0 + 4 * (l >> 4) + i, tc = t0 + 16 * u + (l & 15);  // row = expert, column = token
+    if (er < a.E && tc < a.T) a.logits[(int64_t)tc * a.E + er] = v;
   }
 }
 
+template <int TT, int NB>
+__global__ __launch_bounds__(256) void k_router_split(RouterSplitArgs a) {
+  constexpr int W = 4;
+  __shared__ v4f s_part[W][TT][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * TT, slice = blockIdx.z;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const uint16_t* wrow = a.wr + (int64_t)min(e0 + r16, a.E - 1) * a.H + 8 * g4;
+  const uint16_t* xrow[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) xrow[u] = a.x + (int64_t)min(t0 + 16 * u + r16, a.T - 1) * a.H + 8 * g4;
+  const int steps = a.H / 32;
+  const int s_begin = (int)((int64_t)steps * slice / a.ks), s_end = (int)((int64_t)steps * (slice + 1) / a.ks);
+  v4f acc[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  int s0 = s_begin + wave;
+  for (; s0 + (NB - 1) * W < s_end; s0 += W * NB) {
+    u32x4 wa[NB], xb[NB][TT];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t off = (int64_t)(s0 + i * W) * 32;
+      wa[i] = gload16(wrow + off);
+#pragma unroll
+      for (int u = 0; u < TT; ++u) xb[i][u] = gload16(xrow[u] + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(wa[i]), as_v8s(xb[i][u]), acc[u], 0, 0, 0);
+  }
+  for (; s0 < s_end; s0 += W) {
+    const int64_t off = (int64_t)s0 * 32;
+    const u32x4 wa = gload16(wrow + off);
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(wa), as_v8s(gload16(xrow[u] + off)), acc[u], 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < TT; ++u) s_part[wave][u][lane] = acc[u];
+  __syncthreads();
+  float* out = a.partial + (int64_t)slice * a.T * a.E;
+  for (int idx = threadIdx.x; idx < TT * 64 * 4; idx += 64 * W) {
+    const int u = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
+    const float v = ((s_part[0][u][l][i] + s_part[1][u][l][i]) + s_part[2][u][l][i]) + s_part[3][u][l][i];
+    const int er = e0 + 4 * (l >> 4) + i, tc = t0 + 16 * u + (l & 15);
+    if (er < a.E && tc < a.T) out[(int64_t)tc * a.E + er] = v;
+  }
+}
+
+// Order-preserving key: for non-NaN floats, a < b  <=>  key(a) < key(b), and +0 and -0
+// (equal as floats) share one key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f == 0.f ? 0.f : f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+
 __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;  // whole waves
+  __shared__ uint32_t s_key[4][MOE_MAX_TOPK];
+  __shared__ int s_id[4][MOE_MAX_TOPK];
+  __shared__ float s_val[4][MOE_MAX_TOPK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = min(blockIdx.x * 4 + wave, a.T - 1);  // spare waves redo the last token, not stored
+  const bool store = blockIdx.x * 4 + wave < a.T;
   const float* z = a.logits + (int64_t)t * a.E;
+  const int64_t slice_stride = (int64_t)a.T * a.E;
   float v[4];
-  bool taken[4];
+  uint32_t key[4];
+  // every partial sum's load is issued before the first addition (columns past E read
+  // column E - 1 and are dropped); then the sums are taken in slice order
+  float part[4][kGateMaxSplit];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = min(lane + 64 * j, a.E - 1);
+#pragma unroll
+    for (int s = 0; s < kGateMaxSplit; ++s) part[j][s] = s < a.ks ? z[s * slice_stride + e] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < a.E ? z[e] : -INFINITY;
-    taken[j] = e >= a.E;
+    float zz = part[j][0];
+#pragma unroll
+    for (int s = 1; s < kGateMaxSplit; ++s)
+      if (s < a.ks) zz += part[j][s];
+    if (e < a.E && a.logits_out && store) a.logits_out[(int64_t)t * a.E + e] = zz;
+    v[j] = e < a.E ? zz : 0.f;
+    key[j] = e < a.E ? order_key(zz) : 0u;  // below every real logit's key (k <= E)
   }
-  float zsel = 0.f, zmax = 0.f, sum = 0.f;
-  int myid = -1;
-  float myz = 0.f;
-  for (int r = 0; r < a.k; ++r) {
-    // this lane's best untaken (largest logit, then lowest id: j ascending is id ascending)
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  // thr = the largest key with at least k keys >= it, i.e. the k-th largest key
+  uint32_t thr = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = thr | (1u << b);
+    int n = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (!taken[j] && (v[j] > bv || bi == 0x7FFFFFFF)) {
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
-    // wave argmax by (value desc, id asc)
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == bi) taken[j] = true;
-    zsel = bv;
-    if (r == 0) zmax = bv;
-    const float ex = expf(zsel - zmax);
-    sum += ex;
-    if (lane == r) {
-      myid = bi;
-      myz = zsel;
-    }
+    for (int j = 0; j < 4; ++j) n += wave_count(key[j] >= c);
+    if (n >= a.k) thr = c;
   }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gt += wave_count(key[j] > thr);
+  // keys equal to thr fill the remaining k - gt places in expert-id order (j, then lane)
+  int eq_left = a.k - gt, slot = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t meq = __ballot(key[j] == thr);
+    const int before_eq = __popcll(meq & below);
+    const bool sel = key[j] > thr || (key[j] == thr && before_eq < eq_left);
+    const uint64_t msel = __ballot(sel);
+    if (sel) {
+      const int p = slot + __popcll(msel & below);
+      s_key[wave][p] = key[j];
+      s_id[wave][p] = lane + 64 * j;
+      s_val[wave][p] = v[j];
+    }
+    slot += __popcll(msel);
+    eq_left -= min(eq_left, __popcll(meq));
+  }
+  __syncthreads();
   if (lane < a.k) {
-    a.ids[(int64_t)t * a.k + lane] = myid;
-    a.w[(int64_t)t * a.k + lane] = expf(myz - zmax) / sum;
+    const uint32_t mk = s_key[wave][lane];
+    const int mid = s_id[wave][lane];
+    const float mv = s_val[wave][lane];
+    int rank = 0;
+    float zmax = -INFINITY;
+    for (int p = 0; p < a.k; ++p) {
+      const uint32_t ok = s_key[wave][p];
+      rank += ok > mk || (ok == mk && s_id[wave][p] < mid);
+      zmax = fmaxf(zmax, s_val[wave][p]);
+    }
+    float sum = 0.f;
+    for (int p = 0; p < a.k; ++p) sum += expf(s_val[wave][p] - zmax);
+    if (store) {
+      a.ids[(int64_t)t * a.k + rank] = mid;
+      a.w[(int64_t)t * a.k + rank] = expf(mv - zmax) / sum;
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_router, dim3((a.E + 15) / 16, (a.T + 15) / 16), dim3(256), 0, st, a);
+  // Enough workgroups to cover the CUs with 16-token tiles when T is small; wider token
+  // tiles cut the L2 re-reads of the router weights once there are tokens to spare.
+  const int eb = (a.E + 15) / 16;
+  if ((int64_t)eb * ((a.T + 63) / 64) >= 256)
+    hipLaunchKernelGGL((k_router<4, 8, 6>), dim3(eb, (a.T + 63) / 64), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_router<1, 16, 7>), dim3(eb, (a.T + 15) / 16), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+int gate_split(int T, int H, int E) {
+  // Token tiles of up to 128 tokens; split K until about 256 workgroups are in flight, with
+  // at least 8 K steps (two per wave) in every slice.
+  const int tiles = ((E + 15) / 16) * ((T + 127) / 128);
+  const int ks = (256 + tiles - 1) / tiles;
+  return std::max(1, std::min({ks, kGateMaxSplit, H / 256}));
+}
+
+hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st) {
+  const int eb = (a.E + 15) / 16;
+  if (a.T > 64)
+    hipLaunchKernelGGL((k_router_split<8, 3>), dim3(eb, (a.T + 127) / 128, a.ks), dim3(256), 0, st, a);
+  else if (a.T > 32)
+    hipLaunchKernelGGL((k_router_split<4, 5>), dim3(eb, 1, a.ks), dim3(256), 0, st, a);
+  else if (a.T > 16)
+    hipLaunchKernelGGL((k_router_split<2, 8>), dim3(eb, 1, a.ks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_router_split<1, 8>), dim3(eb, 1, a.ks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

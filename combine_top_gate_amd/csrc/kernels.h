@@ -132,10 +132,23 @@ struct RouterArgs {
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
 
+// Split-K router: partial[s][t][e] = sum over K slice s of x[t][h] * wr[e][h].
+struct RouterSplitArgs {
+  const uint16_t* x;   // [T][H] bf16
+  const uint16_t* wr;  // [E][H] bf16
+  float* partial;      // [ks][T][E]
+  int T, H, E, ks;
+};
+// The split (ks) and token-tile width the fused gate uses for a shape; ks <= kGateMaxSplit.
+constexpr int kGateMaxSplit = 16;
+int gate_split(int T, int H, int E);
+hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st);
+
 struct TopkArgs {
-  const float* logits;  // [T][E], E <= 256
+  const float* logits;  // [ks][T][E] fp32 partial sums, added in slice order; E <= 256
+  float* logits_out;    // [T][E] the sums, or NULL (only with ks > 1)
   int32_t* ids;         // [T][k]
   float* w;             // [T][k]
-  int T, E, k;
+  int T, E, k, ks;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);

@@ -277,6 +277,22 @@ moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const void* x, con
 moe_status moe_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits, int32_t* ids, float* w,
                             hipStream_t stream);
 
+/*
+ * moe_gate: the two steps above in one call, for the latency of small batches: the router's
+ * K reduction is split over workgroups so that a few hundred tokens still occupy every CU.
+ * Partial sums go to `workspace` (device, 16-byte aligned, caller-owned, at least
+ * moe_gate_workspace_bytes(T, H, E) bytes given in workspace_bytes; its contents on entry
+ * do not matter and are overwritten) and are added in a fixed order, so the result does
+ * not depend on timing.  logits [T][E] fp32 receives the sums when not NULL; ids and w are
+ * as for moe_topk_softmax, and are the top-k of exactly those sums.  Same argument rules
+ * as the two calls; a short workspace is MOE_ERR_INVALID_ARG.  The sums' order differs
+ * from moe_router_logits', so the two may differ in the last bits.
+ * moe_gate_workspace_bytes returns 0 for empty or invalid sizes.
+ */
+size_t moe_gate_workspace_bytes(int32_t T, int32_t H, int32_t E);
+moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, void* workspace,
+                    size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream);
+
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 

@@ -114,3 +114,28 @@ def test_topk_softmax_rejects_bad_arguments(lib, T, E, k, lg, ids, w, needle):
 def test_gate_calls_with_no_tokens_are_no_ops(lib):
     assert lib.moe_router_logits(0, 256, 8, None, None, None, None) == binding.MOE_OK
     assert lib.moe_topk_softmax(0, 8, 2, None, None, None, None) == binding.MOE_OK
+
+
+def test_gate_workspace_sizes(lib):
+    # 128 tokens x 256 experts: 16 tiles of 16 experts x 128 tokens, so K is split 16 ways
+    assert lib.moe_gate_workspace_bytes(128, 7168, 256) == 16 * 128 * 256 * 4
+    # 4096 tokens already give 512 tiles: no split
+    assert lib.moe_gate_workspace_bytes(4096, 7168, 256) == 4096 * 256 * 4
+    # a short K cannot be split below 8 steps per slice
+    assert lib.moe_gate_workspace_bytes(8, 256, 8) == 8 * 8 * 4
+    for bad in ((0, 256, 8), (4, 0, 8), (4, 256, 0), (-1, 256, 8)):
+        assert lib.moe_gate_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("T,H,E,k,ws,nbytes,needle", [
+    (4, 100, 8, 2, _A16, 1 << 20, "H"),
+    (4, 256, 300, 2, _A16, 1 << 20, "E"),
+    (4, 256, 8, 9, _A16, 1 << 20, "k"),
+    (4, 256, 8, 2, None, 1 << 20, "NULL"),
+    (4, 256, 8, 2, _A4, 1 << 20, "aligned"),
+    (4, 256, 8, 2, _A16, 4 * 8 * 4 - 4, "workspace"),
+])
+def test_fused_gate_rejects_bad_arguments(lib, T, H, E, k, ws, nbytes, needle):
+    st = lib.moe_gate(T, H, E, k, _A16, _A16, ws, nbytes, None, _A16, _A16, None)
+    assert st == binding.MOE_ERR_INVALID_ARG
+    assert needle in lib.moe_last_error_message().decode()

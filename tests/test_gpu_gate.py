@@ -9,11 +9,12 @@ Bars:
               -inf logit's weight is 0 on both sides): the kernel
               forms z_j - z_max in fp32 (relative error <= u * spread carried into
               exp), expf (a few ulp), a k-term fp32 sum and one division.
-  logits      |g - r| <= gamma_n * sum_h |x_h * w_h| + 2^-60, n = 32 + H / 128 + 4:
+  logits      |g - r| <= gamma_n * sum_h |x_h * w_h| + 2^-60, n = 32 + ceil(H / 256) + 16:
               bf16 x bf16 products are exact in fp32; a 32-deep MFMA step is
-              counted as 32 sequential fp32 additions, each of the 4 waves chains
-              H / 128 steps, and 4 partial sums are added (Higham, gamma_n = n u /
-              (1 - n u), u = 2^-24).
+              counted as 32 sequential fp32 additions; the K steps are split over
+              at least 8 waves (so a wave chains at most ceil(H / 256) of them) and
+              at most 16 partial sums are added (Higham, gamma_n = n u / (1 - n u),
+              u = 2^-24).
   end to end  ids equal the oracle's wherever the gap between the k-th and the
               (k+1)-th fp64 logit exceeds twice the logits bound; everywhere, the
               ids are the exact top-k of the GPU's own logits.
@@ -90,12 +91,14 @@ def router_case(T, H, E, seed):
     x, wr = codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits)
     r = gating.router_logits(x, wr)
     mag = gating.router_logits(np.abs(x), np.abs(wr))
-    bound = gamma(32 + H // 128 + 4) * mag + 2.0 ** -60
+    bound = gamma(32 + -(-H // 256) + 16) * mag + 2.0 ** -60
     return g, r, bound
 
 
 @pytest.mark.parametrize("T,H,E", [(1, 32, 1), (5, 64, 7), (17, 96, 33), (40, 512, 64),
-                                   (33, 1056, 250), (130, 2048, 256)])
+                                   (33, 1056, 250), (130, 2048, 256),
+                                   # wide token tiles (enough tiles to cover the CUs), ragged T and E
+                                   (1000, 256, 256), (2050, 96, 130)])
 def test_router_logits_within_fp32_bound(lib, T, H, E):
     g, r, bound = router_case(T, H, E, seed=T * 131 + E)
     err = np.abs(g - r)
@@ -128,3 +131,49 @@ def test_gate_calls_after_empty_batch(lib):
                                torch.zeros((16, 64), dtype=torch.int16, device="cuda"))
     assert lg.shape == (0, 16)
     check_topk(np.arange(32, dtype=np.float32)[None, :].repeat(3, 0), 4)
+
+
+# ---------------------------------------------------------------- fused gate
+def fused_bound(H, mag):
+    # per wave at most ceil(H / 128) chained MFMA steps (K split over >= 1 slice x 4 waves),
+    # 4 wave partials, at most 16 slice partials
+    return gamma(32 + -(-H // 128) + 4 + 16) * mag + 2.0 ** -60
+
+
+@pytest.mark.parametrize("T,H,E,k", [(1, 256, 8, 2), (5, 1056, 100, 4), (16, 512, 256, 8), (17, 7168, 256, 8),
+                                     (40, 2048, 64, 6), (64, 768, 33, 3), (65, 4096, 256, 8),
+                                     (128, 7168, 256, 8), (130, 1024, 256, 16), (300, 7168, 32, 8),
+                                     (1024, 7168, 256, 8), (2, 64, 1, 1)])
+def test_fused_gate_matches_oracle(lib, T, H, E, k):
+    ri = synth.make_router_inputs(T, H, E, seed=7 * T + H + E)
+    x, wr = dev_bits(ri.x_bits), dev_bits(ri.wr_bits)
+    # a workspace full of NaN: its contents on entry must not matter
+    ws = torch.full((binding.gate_workspace_bytes(T, H, E) // 4 + 4,), float("nan"), device="cuda")
+    ids, w, lg = binding.gate(x, wr, k, workspace=ws, want_logits=True)
+    ids2, w2 = binding.gate(x, wr, k)
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy().astype(np.float64)
+    xd, wd = codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits)
+    r = gating.router_logits(xd, wd)
+    bound = fused_bound(H, gating.router_logits(np.abs(xd), np.abs(wd)))
+    err = np.abs(lg - r)
+    print(f"  T {T} H {H} E {E}: logits max err/bound {np.max(err / bound):.3f}", flush=True)
+    assert np.all(err <= bound)
+    # the ids and weights are exactly the top-k softmax of the returned sums
+    rid, rw = gating.softmax_topk(lg, k)
+    g_ids, g_w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_ids, rid)
+    sel = np.take_along_axis(lg, rid.astype(np.int64), axis=1)
+    spread = np.max(sel[:, :1] - sel, axis=1, keepdims=True)
+    assert np.all(np.abs(g_w - rw) <= (2 * spread + k + 6) * U * rw + 2.0 ** -40)
+    # without the logits output: the same bits
+    assert torch.equal(ids2, ids) and torch.equal(w2, w)
+
+
+def test_fused_gate_short_workspace_rejected(lib):
+    T, H, E = 128, 7168, 256
+    x = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    wr = torch.zeros((E, H), dtype=torch.int16, device="cuda")
+    ws = torch.empty(binding.gate_workspace_bytes(T, H, E) // 4 - 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.MoeError, match="workspace"):
+        binding.gate(x, wr, 8, workspace=ws)
