@@ -133,6 +133,22 @@ def time_gate(torch, binding, synth, T, H, k, calls=200):
             "method": f"{calls} back-to-back calls queued behind a GPU spin, HIP events"}
 
 
+def measure_fp8_mfma(torch, binding, blocks=2048, iters=2000, reps=3):
+    """Sustained FP8 MFMA rate (TFLOP/s) of the library's register-only MFMA probe, best
+    of `reps` launches timed with HIP events on the launch stream."""
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    binding.mfma_fp8_probe(sink, blocks, 10)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = binding.mfma_fp8_probe(sink, blocks, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
 def cpu_baseline(inp, n_experts, repeats):
     """The oracle as it stands, timed on a bounded sample of the same workload.
 
@@ -262,6 +278,9 @@ def main():
         "combine_GBps": round(gbps(nbytes["combine"], avg[3]), 1),
         "gemm_TFLOPs": round(flops / ((avg[1] + avg[2]) * 1e-3) / 1e12, 2),
         "layer_hbm_frac": round(gbps(nbytes["layer"], ms_step) / HBM_PEAK_GBPS, 4),
+        "fractions": {"dispatch_of_hbm": round(gbps(nbytes["dispatch"], avg[0]) / HBM_PEAK_GBPS, 4),
+                      "combine_of_hbm": round(gbps(nbytes["combine"], avg[3]) / HBM_PEAK_GBPS, 4),
+                      "gemm_of_fp8_peak": round(flops / ((avg[1] + avg[2]) * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)},
         "us_per_step_with_stage_events": round((t3 - t2) * 1e6 / args.steps, 2),
         "algorithmic_bytes": nbytes,
         "roofline": {"kernel": "gemm1 (FP8 grouped GEMM + SwiGLU + requant)", "bound": "hbm",
@@ -269,6 +288,9 @@ def main():
                      "frac": round(g1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes["gemm1"]},
     }
+    mfma = measure_fp8_mfma(torch, binding)
+    rec["fp8_mfma_measured_TFLOPs"] = mfma
+    rec["fractions"]["gemm_of_measured_fp8_mfma"] = round(rec["gemm_TFLOPs"] / mfma, 4)
     if not args.no_gate:
         print("[bench] gate timing", file=sys.stderr, flush=True)
         rec["gate_us"] = time_gate(torch, binding, synth, inp.S * inp.T_s, inp.H, inp.k)

@@ -58,7 +58,7 @@ _lib = None
 def header_functions():
     """Names of the functions declared in include/ctg_moe.h."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\s*\*)\s*(moe_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\s*\*|size_t|int64_t)\s*(moe_\w+)\s*\(", text, re.M)))
 
 
 def load():
@@ -89,6 +89,7 @@ def load():
         "moe_router_logits": (st, [I32, I32, I32, VP, VP, VP, VP]),
         "moe_topk_softmax": (st, [I32, I32, I32, VP, VP, VP, VP]),
         "moe_gate_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32]),
+        "moe_mfma_fp8_probe": (ctypes.c_int64, [VP, I32, I32, VP]),
         "moe_gate": (st, [I32, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP, VP, VP, VP]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
@@ -148,6 +149,14 @@ def gate(x, wr, k, workspace=None, want_logits=False):
     _check(lib.moe_gate(T, H, E, k, _ptr(x), _ptr(wr), _ptr(workspace), nbytes, _ptr(logits), _ptr(ids),
                         _ptr(w), _stream()))
     return (ids, w, logits) if want_logits else (ids, w)
+
+
+def mfma_fp8_probe(sink, blocks, iters):
+    """Launch the FP8 MFMA probe on the current stream; returns the flops it performs."""
+    flops = load().moe_mfma_fp8_probe(_ptr(sink), blocks, iters, _stream())
+    if flops < 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, _lib.moe_last_error_message().decode())
+    return flops
 
 
 def gate_workspace_bytes(T, H, E):

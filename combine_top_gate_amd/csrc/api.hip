@@ -736,6 +736,18 @@ moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, c
   return MOE_OK;
 }
 
+int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream_t stream) {
+  if (!sink || ((uintptr_t)sink & 3u) || blocks < 1 || iters < 1) {
+    fail(MOE_ERR_INVALID_ARG, "sink must be a 4-byte aligned device pointer; blocks, iters >= 1");
+    return -1;
+  }
+  if (launch_mfma_fp8_probe(sink, blocks, iters, stream) != hipSuccess) {
+    fail(MOE_ERR_HIP, "probe launch failed");
+    return -1;
+  }
+  return (int64_t)blocks * 4 * iters * mfma_fp8_probe_chains() * (2 * 16 * 16 * 128);
+}
+
 moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {
   if (!c || !bits) return fail(MOE_ERR_INVALID_ARG, "ctx or bits is NULL");
   HIP_TRY(hipDeviceSynchronize());

@@ -152,3 +152,7 @@ struct TopkArgs {
   int T, E, k, ks;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+// ---- measurement aid ----------------------------------------------------------
+hipError_t launch_mfma_fp8_probe(float* sink, int blocks, int iters, hipStream_t st);
+int mfma_fp8_probe_chains();

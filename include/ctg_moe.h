@@ -293,6 +293,17 @@ size_t moe_gate_workspace_bytes(int32_t T, int32_t H, int32_t E);
 moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, void* workspace,
                     size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream);
 
+/*
+ * Measurement aid, not part of the layer: launches `blocks` workgroups that issue only
+ * FP8 MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4, operands in registers, no memory
+ * traffic) `iters` times per chain, and returns the flops the launch performs (-1 on
+ * invalid arguments: sink NULL or not 4-byte aligned, blocks or iters < 1).  sink:
+ * device fp32 [4], caller-owned, accumulated into (its contents are not meaningful).
+ * The caller times the launch on `stream`; flops / time is the sustained FP8 MFMA rate,
+ * reported beside the published peak.
+ */
+int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream_t stream);
+
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 

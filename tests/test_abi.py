@@ -139,3 +139,10 @@ def test_fused_gate_rejects_bad_arguments(lib, T, H, E, k, ws, nbytes, needle):
     st = lib.moe_gate(T, H, E, k, _A16, _A16, ws, nbytes, None, _A16, _A16, None)
     assert st == binding.MOE_ERR_INVALID_ARG
     assert needle in lib.moe_last_error_message().decode()
+
+
+def test_mfma_probe_rejects_bad_arguments(lib):
+    assert lib.moe_mfma_fp8_probe(None, 4, 4, None) == -1
+    assert lib.moe_mfma_fp8_probe(ctypes.c_void_p(0x10002), 4, 4, None) == -1
+    assert lib.moe_mfma_fp8_probe(_A16, 0, 4, None) == -1
+    assert lib.moe_mfma_fp8_probe(_A16, 4, 0, None) == -1
