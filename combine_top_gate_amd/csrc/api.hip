@@ -193,7 +193,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (e = alloc(&c->y, (size_t)c->rows_cap * H * (f32 ? 4 : 2))) != hipSuccess ||
       (e = alloc((void**)&c->cnt, (size_t)S * E * 4)) != hipSuccess ||
       (e = alloc((void**)&c->off, (size_t)S * E * 4)) != hipSuccess ||
-      (e = alloc((void**)&c->dst_row, (size_t)S * Tc * k * 4)) != hipSuccess ||
+      // + MOE_MAX_TOPK entries: the combine reads a token's row map as whole vectors of
+      // 2, 4, 8 or 16 entries, past the last token's k (never used)
+      (e = alloc((void**)&c->dst_row, ((size_t)S * Tc * k + MOE_MAX_TOPK) * 4)) != hipSuccess ||
       (e = alloc((void**)&c->row_src, (size_t)c->R_cap * 4)) != hipSuccess ||
       (e = alloc((void**)&c->err, 4)) != hipSuccess ||
       (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess ||

@@ -3,29 +3,49 @@
 // expert windows are read where they are and nothing is restored in between
 // ("Relay Buffer Independent Communication over Pooled HBM for Efficient MoE
 // Inference on Ascend", abstract: direct reading from expert windows).
-// Each thread owns one 16-byte piece of a token row: 8 bf16 or 4 fp32 values.
+// Each thread owns one 16-byte piece of a token row: 8 bf16 or 4 fp32 values.  k <= 16.
 #include "kernels.h"
 
 namespace {
 
-template <bool F32>
+// KM >= k row slots are loaded (a slot past k, or with no row, loads row 0 and is not
+// added), so the loads carry no condition and are all in flight together; then the rows
+// are added in slot order, the shared expert's (weight 1) last.
+template <bool F32, int KM, bool SH>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   constexpr int V = F32 ? 4 : 8;
   const int tok = blockIdx.x;
   const int c = (blockIdx.y * 256 + threadIdx.x) * V;
   if (c >= a.H) return;
+  const uint8_t* ybase = static_cast<const uint8_t*>(a.y) + (int64_t)c * (F32 ? 4 : 2);
+  const int64_t ystride = (int64_t)a.H * (F32 ? 4 : 2);
+  // the token's row map and weights are the same for the whole workgroup (scalar loads);
+  // the row map is read as KM consecutive entries (its buffer has MOE_MAX_TOPK entries of
+  // padding past the last token), the weights only up to k
+  const int32_t* rmap = a.dst_row + (int64_t)tok * a.k;
+  const float* wmap = a.topk_w + (int64_t)tok * a.k;
+  int rows[KM];
+  float wts[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = j < a.k ? rmap[j] : -1;
+    wts[j] = wmap[min(j, a.k - 1)];
+  }
+  uint4 yv[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) yv[j] = *reinterpret_cast<const uint4*>(ybase + max(rows[j], 0) * ystride);
+  uint4 ysh;
+  if constexpr (SH) ysh = *reinterpret_cast<const uint4*>(ybase + (int64_t)(a.R + tok) * ystride);
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  auto add_row = [&](int r, float w) {
+  auto add = [&](const uint4& y, float w) {
     if constexpr (F32) {
-      const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.y) + (int64_t)r * a.H + c);
-      acc[0] = fmaf(w, y.x, acc[0]);
-      acc[1] = fmaf(w, y.y, acc[1]);
-      acc[2] = fmaf(w, y.z, acc[2]);
-      acc[3] = fmaf(w, y.w, acc[3]);
+      acc[0] = fmaf(w, __uint_as_float(y.x), acc[0]);
+      acc[1] = fmaf(w, __uint_as_float(y.y), acc[1]);
+      acc[2] = fmaf(w, __uint_as_float(y.z), acc[2]);
+      acc[3] = fmaf(w, __uint_as_float(y.w), acc[3]);
     } else {
-      const uint4 y = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.y) + (int64_t)r * a.H + c);
       const uint32_t u[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -34,11 +54,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       }
     }
   };
-  for (int j = 0; j < a.k; ++j) {
-    const int r = a.dst_row[(int64_t)tok * a.k + j];
-    if (r >= 0) add_row(r, a.topk_w[(int64_t)tok * a.k + j]);
-  }
-  if (a.has_shared) add_row(a.R + tok, 1.0f);
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (rows[j] >= 0) add(yv[j], wts[j]);  // uniform
+  if constexpr (SH) add(ysh, 1.0f);
   if constexpr (F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (int64_t)tok * a.H + c) =
         make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -52,14 +71,26 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
 }
 
+template <bool F32, bool SH>
+void launch_km(const CombineArgs& a, dim3 grid, hipStream_t st) {
+  if (a.k <= 2)
+    hipLaunchKernelGGL((k_combine<F32, 2, SH>), grid, dim3(256), 0, st, a);
+  else if (a.k <= 4)
+    hipLaunchKernelGGL((k_combine<F32, 4, SH>), grid, dim3(256), 0, st, a);
+  else if (a.k <= 8)
+    hipLaunchKernelGGL((k_combine<F32, 8, SH>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_combine<F32, MOE_MAX_TOPK, SH>), grid, dim3(256), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int V = a.out_f32 ? 4 : 8;
   const dim3 grid(a.T, (a.H + 256 * V - 1) / (256 * V));
   if (a.out_f32)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, a);
+    a.has_shared ? launch_km<true, true>(a, grid, st) : launch_km<true, false>(a, grid, st);
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, a);
+    a.has_shared ? launch_km<false, true>(a, grid, st) : launch_km<false, false>(a, grid, st);
   return hipGetLastError();
 }
