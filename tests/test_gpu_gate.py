@@ -177,3 +177,35 @@ def test_fused_gate_short_workspace_rejected(lib):
     ws = torch.empty(binding.gate_workspace_bytes(T, H, E) // 4 - 1, dtype=torch.float32, device="cuda")
     with pytest.raises(binding.MoeError, match="workspace"):
         binding.gate(x, wr, 8, workspace=ws)
+
+
+def test_gate_drives_the_layer(lib):
+    """The gate ahead of dispatch: the GPU gate's ids and weights go device to device into
+    the layer.  The oracle runs its own gate (fp64 router logits, top-k softmax) on the
+    same bf16 router inputs and its layer on its own ids and weights; wherever the two
+    gates chose the same ids, the layer outputs agree to the FP8 criterion (the gates'
+    weights differ only by fp32 rounding)."""
+    from oracle import layer
+    from test_gpu_parity import close, out_np
+    inp = synth.make_inputs("decode128_fp8", S=4, T_s=16, H=1024, I=256, E=32, k=8, seed=71)
+    S, T_s, k = inp.S, inp.T_s, inp.k
+    T = S * T_s
+    ri = synth.make_router_inputs(T, inp.H, inp.E, seed=72)
+    ids, w = binding.gate(dev_bits(ri.x_bits), dev_bits(ri.wr_bits), k)
+    moe = binding.Moe.for_inputs(inp)
+    d = binding.DeviceInputs(inp)
+    d.ids = ids.view(S, T_s, k)
+    d.topk_w = w.view(S, T_s, k)
+    moe.run(d)
+    torch.cuda.synchronize()
+    # the oracle's gate and layer, from the generator's inputs only
+    r = gating.router_logits(codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits))
+    rid, rw = gating.softmax_topk(r, k)
+    inp.ids = rid.reshape(S, T_s, k).astype(np.int32)
+    inp.topk_w = rw.astype(np.float32).reshape(S, T_s, k)
+    ref = layer.moe_layer(inp)
+    same = np.all(ids.cpu().numpy() == rid, axis=1)
+    print(f"  {int(same.sum())} of {T} tokens routed alike", flush=True)
+    assert same.mean() > 0.9
+    g = out_np(inp, d.out).reshape(T, inp.H)
+    assert close(g[same], np.asarray(ref["out"]).reshape(T, inp.H)[same], 2e-2)
