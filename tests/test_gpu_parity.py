@@ -216,6 +216,11 @@ def check_routing(g, ref):
 
 SMALL = [
     ("tiny_f32", {}, False),
+    # the most slots per token (16), an odd k between the combine's slot counts, and k = 1
+    # with the shared expert
+    ("decode128_fp8", dict(S=2, T_s=5, H=256, I=128, E=20, k=16, seed=15), False),
+    ("tiny_f32", dict(E=9, k=5, seed=17), False),
+    ("decode256_mxfp4_shared", dict(S=3, T_s=4, H=256, I=128, E=6, k=1, shared_I=128, seed=16), True),
     ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=11), False),
     ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=11), True),
     ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=12), False),
