@@ -198,8 +198,8 @@ def _cpu_once(inp, n_experts):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not "
-              "part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer on one GPU; it has no multi-GPU "
+              "mode (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     from combine_top_gate_amd import binding, synth

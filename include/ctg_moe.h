@@ -92,7 +92,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or dtype combination */
-  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request the library does not implement */
   MOE_ERR_HIP = 3,         /* a HIP runtime call failed (no device, out of memory, ...) */
   MOE_ERR_DEVICE = 4       /* a device-side condition was latched; see moe_last_device_error */
 } moe_status;
