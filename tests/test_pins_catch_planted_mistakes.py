@@ -1,0 +1,90 @@
+"""The oracle's pins are strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/ (a swapped operand, a shifted scale
+block, a wrong divisor, an off-by-one exponent, a dropped term, a wrong tie rule, ...)
+and runs the oracle's pin tests (tests/test_oracle_*.py) against the copy in a separate
+process: at least one pin must fail.  The unmodified copy must pass, so a failure is the
+planted mistake's doing and not the copy's.  Only the oracle's CPU code is changed.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (file in oracle/, original text, planted text)
+MISTAKES = [
+    ("layer.py", "return silu(a[:, :inter]) * a[:, inter:2 * inter]",
+     "return silu(a[:, inter:2 * inter]) * a[:, :inter]"),                       # gate/up swapped
+    ("layer.py", "kb * BLOCK:(kb + 1) * BLOCK] * s[nb, kb])",
+     "kb * BLOCK:(kb + 1) * BLOCK] * s[nb, (kb + 1) % s.shape[1]])"),            # scale block shifted
+    ("layer.py", "s = codecs.fp32_round(amax / codecs.E4M3_MAX)",
+     "s = codecs.fp32_round(amax / 447.0)"),                                     # wrong divisor
+    ("layer.py", "acc += float(topk_w[s, t, j]) * y_win[r]",
+     "acc += float(topk_w[s, t, (j + 1) % k]) * y_win[r]"),                      # wrong slot weight
+    ("layer.py", "            off[s, e] = running\n            running += cnt[s, e]",
+     "            running += cnt[s, e]\n            off[s, e] = running"),          # inclusive prefix
+    ("codecs.py", "mag = (1.0 + man / 8.0) * 2.0 ** (exp - 7)",
+     "mag = (1.0 + man / 8.0) * 2.0 ** (exp - 8)"),                              # e4m3 bias 8
+    ("codecs.py", "r = np.round(m * 256.0)", "r = np.trunc(m * 256.0)"),        # truncating rounding
+    ("codecs.py", "steps = np.round(mag / quantum)", "steps = np.floor(mag / quantum + 0.5)"),  # ties away
+    ("layer.py", "        for s in range(S):\n            base",
+     "        for s in reversed(range(S)):\n            base"),                    # sources reversed
+    ("layer.py", "                acc += y_shared[s * T_s + t]",
+     "                acc += 0 * y_shared[s * T_s + t]"),                         # shared expert dropped
+    ("layer.py", "v[:, b * MX_BLOCK:(b + 1) * MX_BLOCK] * s[:, b:b + 1]",
+     "v[:, b * MX_BLOCK:(b + 1) * MX_BLOCK] * s[:, (b + 1) % s.shape[1]:(b + 1) % s.shape[1] + 1]"),  # e8m0 shifted
+    ("layer.py", "        s = np.where(amax == 0, 1.0, s)", "        s = np.where(amax == 0, 0.5, s)"),
+    ("layer.py", "                r = s * seg + off[s, e] + placed[e]",
+     "                r = s * seg + off[s, e] + cnt[s, e] - 1 - placed[e]"),      # unstable bucket order
+    ("layer.py", "    a = x @ w13.T", "    a = x @ w13.T * 1.0000001"),           # tiny scale error
+    ("layer.py", "        v = np.clip(v, -codecs.E4M3_MAX, codecs.E4M3_MAX)",
+     "        v = np.clip(v, -codecs.E4M3_MAX, codecs.E4M3_MAX) * 1.01"),
+    ("layer.py", "    y = h_used @ w2.T", "    y = h @ w2.T"),                      # requantisation skipped
+    ("gating.py", "key=lambda e: (-logits[t, e], e)", "key=lambda e: (-logits[t, e], -e)"),  # tie rule
+    ("gating.py", "w[t, j] = ex[j] / tot", "w[t, j] = ex[j] / (tot + 1e-9)"),
+    ("codecs.py", "        mag = (man / 8.0) * 2.0 ** (1 - 7)", "        mag = (man / 8.0) * 2.0 ** (0 - 7)"),  # subnormals
+    ("layer.py", "        y_win[r] = round_out(y, inp.out)", "        y_win[r] = y"),  # bf16 rounding of y
+    ("gating.py", "np.asarray(x, dtype=np.float64) @ np.asarray(wr, dtype=np.float64).T",
+     "np.asarray(x, dtype=np.float64) @ np.asarray(wr, dtype=np.float64).T * (1 + 1e-9)"),   # router
+    ("codecs.py", "b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16",
+     "b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15"),          # bf16 decode
+]
+
+
+def _copy(dst):
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(dst, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "combine_top_gate_amd"), os.path.join(dst, "combine_top_gate_amd"),
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so", "_build", "csrc"))
+    os.makedirs(os.path.join(dst, "tests"))
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(dst, "tests", "golden"))
+    pins = sorted(f for f in os.listdir(os.path.join(ROOT, "tests")) if f.startswith("test_oracle"))
+    for f in pins + ["conftest.py"]:
+        shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(dst, "tests", f))
+    return ["tests/" + f for f in pins]
+
+
+def _run_pins(dst, pins):
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *pins],
+                       cwd=dst, capture_output=True, text=True, timeout=600)
+    return r.returncode, (r.stdout.strip().splitlines() or [r.stderr[-300:]])[-1]
+
+
+def test_unmodified_copy_passes(tmp_path):
+    rc, last = _run_pins(str(tmp_path), _copy(str(tmp_path)))
+    assert rc == 0, last
+
+
+@pytest.mark.parametrize("fname,orig,planted", MISTAKES, ids=[f"{m[0]}:{i}" for i, m in enumerate(MISTAKES)])
+def test_planted_mistake_fails_a_pin(tmp_path, fname, orig, planted):
+    pins = _copy(str(tmp_path))
+    p = os.path.join(str(tmp_path), "oracle", fname)
+    src = open(p).read()
+    assert src.count(orig) == 1, "the text to mutate is no longer in the oracle"
+    open(p, "w").write(src.replace(orig, planted))
+    rc, last = _run_pins(str(tmp_path), pins)
+    assert rc == 1 and "failed" in last, last
