@@ -90,6 +90,7 @@ def load():
         "moe_topk_softmax": (st, [I32, I32, I32, VP, VP, VP, VP]),
         "moe_gate_workspace_bytes": (ctypes.c_size_t, [I32, I32, I32]),
         "moe_mfma_fp8_probe": (ctypes.c_int64, [VP, I32, I32, VP]),
+        "moe_mfma_dot16x16": (st, [I32, VP, VP, VP, VP]),
         "moe_gate": (st, [I32, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP, VP, VP, VP]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
@@ -157,6 +158,18 @@ def mfma_fp8_probe(sink, blocks, iters):
     if flops < 0:
         raise MoeError(MOE_ERR_INVALID_ARG, _lib.moe_last_error_message().decode())
     return flops
+
+
+def mfma_dot16x16(a_codes, b_codes, a_fp4=False):
+    """One scaled MFMA with unit scales: out[i][j] = the instruction's own sum of
+    a[i][k] * b[j][k] over 128 k, for a [16][128] e4m3 codes (or e2m1 codes, one per byte,
+    with a_fp4) and b [16][128] e4m3 codes, uint8 on the device; returns fp32 [16][16]."""
+    if tuple(a_codes.shape) != (16, 128) or tuple(b_codes.shape) != (16, 128):
+        raise ValueError("a and b must be [16][128] code arrays")
+    a, b = a_codes.contiguous(), b_codes.contiguous()
+    out = torch.empty((16, 16), dtype=torch.float32, device=a.device)
+    _check(load().moe_mfma_dot16x16(MOE_FP4_E2M1 if a_fp4 else MOE_FP8_E4M3, _ptr(a), _ptr(b), _ptr(out), _stream()))
+    return out
 
 
 def gate_workspace_bytes(T, H, E):

@@ -750,6 +750,14 @@ int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream
   return (int64_t)blocks * 4 * iters * mfma_fp8_probe_chains() * (2 * 16 * 16 * 128);
 }
 
+moe_status moe_mfma_dot16x16(moe_dtype a_fmt, const uint8_t* a, const uint8_t* b, float* out, hipStream_t stream) {
+  if (a_fmt != MOE_FP8_E4M3 && a_fmt != MOE_FP4_E2M1)
+    return fail(MOE_ERR_INVALID_ARG, "a_fmt must be MOE_FP8_E4M3 or MOE_FP4_E2M1");
+  if (!a || !b || !out || ((uintptr_t)out & 3u)) return fail(MOE_ERR_INVALID_ARG, "a, b or out is NULL or out misaligned");
+  HIP_TRY(launch_mfma_dot(a_fmt == MOE_FP4_E2M1, a, b, out, stream));
+  return MOE_OK;
+}
+
 moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {
   if (!c || !bits) return fail(MOE_ERR_INVALID_ARG, "ctx or bits is NULL");
   HIP_TRY(hipDeviceSynchronize());

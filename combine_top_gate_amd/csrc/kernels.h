@@ -156,3 +156,4 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // ---- measurement aid ----------------------------------------------------------
 hipError_t launch_mfma_fp8_probe(float* sink, int blocks, int iters, hipStream_t st);
 int mfma_fp8_probe_chains();
+hipError_t launch_mfma_dot(bool a_fp4, const uint8_t* a, const uint8_t* b, float* out, hipStream_t st);

@@ -304,6 +304,17 @@ moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, c
  */
 int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream_t stream);
 
+/*
+ * Verification aid, not part of the layer: one v_mfma_scale_f32_16x16x128_f8f6f4 with unit
+ * scales -- the instruction the FP8 and MXFP4 GEMMs use -- so that tests can check how it
+ * accumulates.  a: 16 rows of 128 codes in a_fmt (MOE_FP8_E4M3, or MOE_FP4_E2M1 with one
+ * code in the low 4 bits of each byte), b: 16 columns of 128 e4m3 codes; each row or column
+ * is 128 consecutive bytes.  out: fp32 [16][16] with out[i][j] = the instruction's sum over
+ * k of a[i][k] * b[j][k].  All three are caller-owned device buffers.  Another a_fmt, NULL
+ * pointers or a misaligned out return MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_mfma_dot16x16(moe_dtype a_fmt, const uint8_t* a, const uint8_t* b, float* out, hipStream_t stream);
+
 /* Waits for the device, returns the latched device error bits and clears them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 

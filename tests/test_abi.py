@@ -146,3 +146,11 @@ def test_mfma_probe_rejects_bad_arguments(lib):
     assert lib.moe_mfma_fp8_probe(ctypes.c_void_p(0x10002), 4, 4, None) == -1
     assert lib.moe_mfma_fp8_probe(_A16, 0, 4, None) == -1
     assert lib.moe_mfma_fp8_probe(_A16, 4, 0, None) == -1
+
+
+def test_mfma_dot_rejects_bad_arguments(lib):
+    inv = binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_dot16x16(binding.MOE_BF16, _A16, _A16, _A16, None) == inv
+    assert lib.moe_mfma_dot16x16(binding.MOE_FP8_E4M3, None, _A16, _A16, None) == inv
+    assert lib.moe_mfma_dot16x16(binding.MOE_FP4_E2M1, _A16, None, _A16, None) == inv
+    assert lib.moe_mfma_dot16x16(binding.MOE_FP8_E4M3, _A16, _A16, ctypes.c_void_p(0x10002), None) == inv
