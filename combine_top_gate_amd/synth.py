@@ -60,6 +60,10 @@ CONFIGS = {
     "decode256_mxfp4_shared": dict(S=8, T_s=32, H=7168, I=2048, E=32, k=8, act="fp8",
                                    weight="fp4", out="bf16", shared_I=2048, routing="normal",
                                    seed=4),
+    # the same layer with bf16 activations (W4A16): x and h stay bf16
+    "decode256_w4a16_shared": dict(S=8, T_s=32, H=7168, I=2048, E=32, k=8, act="bf16",
+                                   weight="fp4", out="bf16", shared_I=2048, routing="normal",
+                                   seed=5),
 }
 
 
@@ -79,7 +83,7 @@ class LayerInputs:
     logits: np.ndarray                 # fp64 [S*T_s][E]
     ids: np.ndarray                    # int32 [S][T_s][k]
     topk_w: np.ndarray                 # fp32 [S][T_s][k]
-    x: np.ndarray                      # uint8 [S][T_s][H] (fp8) or fp32 [S][T_s][H]
+    x: np.ndarray                      # uint8 [S][T_s][H] (fp8), uint16 bf16 bits or fp32
     x_scale: Optional[np.ndarray]      # fp32 [S][T_s][H/128] or None
     w13: np.ndarray
     s13: Optional[np.ndarray]
@@ -233,6 +237,8 @@ def make_inputs(name="decode128_fp8", **over):
         xq, xs = quant_fp8_rows(xf)
         x = xq.reshape(S, T_s, H)
         x_scale = xs.reshape(S, T_s, H // 128)
+    elif act == "bf16":
+        x, x_scale = _bf16_bits(xf).reshape(S, T_s, H), None
     else:
         x, x_scale = xf.reshape(S, T_s, H), None
     w13, s13 = _gen_weights(seq[4:4 + E], weight, 2 * I, H)

@@ -208,15 +208,30 @@ def requant_1x128(h):
     return codes, scales
 
 
+def h_format(act):
+    """How h is stored between the projections: "fp8" (1x128 requantisation) for FP8
+    activations, "bf16" for bf16 activations (the W4A16 variant), None (as is) for fp32."""
+    return {"fp8": "fp8", "bf16": "bf16"}.get(act)
+
+
 def expert_ffn(x, w13, w2, inter, requant):
     """Dequantised rows x [M][H], W13 [2I][H], W2 [H][I] -> (y [M][H], h_codes, h_scales).
 
-    y = requant(silu(x W13[:I]^T) * (x W13[I:]^T)) W2^T, all in fp64; without
-    requantisation (the fp32 layer) h goes to the down projection as is.
+    y = requant(silu(x W13[:I]^T) * (x W13[I:]^T)) W2^T, all in fp64.  requant: "fp8"
+    (or True) requantises h to FP8 with 1x128 scales; "bf16" rounds h to bf16 (nearest,
+    ties to even), returned as h_codes (fp64 values) with h_scales None; None or False
+    (the fp32 layer) passes h to the down projection as is.  The bf16 form is the W4A16
+    variant: FP4 weights decoded in registers ahead of an MMA that does not take FP4
+    [GC-MoE explainer, "Two MMA Implementations in the Compute Partition"]; the pages do
+    not fix the activations' precision there, and the reading taken is that x and h stay
+    bf16 (h rounded from its exact value).
     """
     a = x @ w13.T
     h = swiglu(a, inter)
-    if requant:
+    if requant == "bf16":
+        hq, hs = codecs.bf16_round(h), None
+        h_used = hq
+    elif requant:
         hq, hs = requant_1x128(h)
         h_used = dequant_act_fp8(hq, hs)
     else:
@@ -269,20 +284,24 @@ def _act_rows(inp):
     if inp.act == "fp8":
         xs = np.asarray(inp.x_scale)
         return dequant_act_fp8(x.reshape(S * T_s, H), xs.reshape(S * T_s, H // BLOCK))
+    if inp.act == "bf16":
+        return codecs.bf16_decode(x.reshape(S * T_s, H))
     return np.asarray(x, dtype=np.float64).reshape(S * T_s, H)
 
 
 def moe_layer(inp):
     """Run the whole layer on the CPU; returns every intermediate the GPU exposes.
 
-    inp has fields: S, T_s, H, I, E, k, act ("f32"|"fp8"), weight
+    inp has fields: S, T_s, H, I, E, k, act ("f32"|"fp8"|"bf16", the last as bf16
+    bit patterns, uint16), weight
     ("f32"|"fp8"|"fp4"), out ("f32"|"bf16"), shared_I (0 = none), x [S][T_s][H],
     x_scale [S][T_s][H/128] or None, ids [S][T_s][k], topk_w [S][T_s][k],
     w13, s13, w2, s2 (per expert, leading dim E) and sh_w13, sh_s13, sh_w2,
     sh_s2 for the shared expert.
     """
     S, T_s, H, I, E, k = inp.S, inp.T_s, inp.H, inp.I, inp.E, inp.k
-    requant = inp.act == "fp8"
+    hfmt = h_format(inp.act)
+    requant = hfmt == "fp8"
     route = dispatch(inp.ids, E)
     rows = expert_rows(route["cnt"], route["off"], T_s, k)
     xt = _act_rows(inp)                       # token-ordered dequantised activations
@@ -291,29 +310,33 @@ def moe_layer(inp):
     y_win = np.zeros((R, H), dtype=np.float64)
     h_codes = np.zeros((R, I), dtype=np.uint8) if requant else None
     h_scales = np.zeros((R, I // BLOCK), dtype=np.float64) if requant else None
+    h_bf16 = np.zeros((R, I), dtype=np.float64) if hfmt == "bf16" else None
     for e in range(E):
         r = rows[e]
         if len(r) == 0:
             continue
         w13 = dequant_weight(inp.weight, inp.w13[e], None if inp.s13 is None else inp.s13[e])
         w2 = dequant_weight(inp.weight, inp.w2[e], None if inp.s2 is None else inp.s2[e])
-        y, hq, hs = expert_ffn(xt[src_token[r]], w13, w2, I, requant)
+        y, hq, hs = expert_ffn(xt[src_token[r]], w13, w2, I, hfmt)
         y_win[r] = round_out(y, inp.out)
         if requant:
             h_codes[r] = hq
             h_scales[r] = hs
+        elif hfmt == "bf16":
+            h_bf16[r] = hq
     y_sh = None
     sh = {}
     if inp.shared_I:
         w13 = dequant_weight(inp.weight, inp.sh_w13, inp.sh_s13)
         w2 = dequant_weight(inp.weight, inp.sh_w2, inp.sh_s2)
-        y_sh, shq, shs = expert_ffn(xt, w13, w2, inp.shared_I, requant)
+        y_sh, shq, shs = expert_ffn(xt, w13, w2, inp.shared_I, hfmt)
         y_sh = round_out(y_sh, inp.out)
-        sh = {"y_shared": y_sh, "h_shared_codes": shq, "h_shared_scales": shs}
+        sh = {"y_shared": y_sh, "h_shared_codes": shq if requant else None, "h_shared_scales": shs,
+              "h_shared_bf16": shq if hfmt == "bf16" else None}
     out = combine(y_win, route["dst_row"], inp.topk_w, y_sh)
     res = dict(route)
     res.update({"expert_rows": rows, "y_win": y_win, "h_codes": h_codes,
-                "h_scales": h_scales, "out": round_out(out, inp.out)})
+                "h_scales": h_scales, "h_bf16": h_bf16, "out": round_out(out, inp.out)})
     res.update(sh)
     return res
 
@@ -347,13 +370,15 @@ def layer_tokens(inp, tokens):
     with no need for the rest of the batch.  Returns fp64 [n][H] rounded to the
     output format.
     """
-    requant = inp.act == "fp8"
+    requant = h_format(inp.act)
     cache = _ExpertCache(inp)
     x = np.asarray(inp.x)
     outs = []
     for s, t in tokens:
         if inp.act == "fp8":
             xt = dequant_act_fp8(x[s, t][None, :], np.asarray(inp.x_scale)[s, t][None, :])
+        elif inp.act == "bf16":
+            xt = codecs.bf16_decode(x[s, t][None, :])
         else:
             xt = np.asarray(x[s, t], dtype=np.float64)[None, :]
         acc = np.zeros(inp.H, dtype=np.float64)

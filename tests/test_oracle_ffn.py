@@ -66,6 +66,33 @@ def test_dense_swiglu_ffn_matches_torch():
     assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)
 
 
+def test_w4a16_ffn_rounds_h_to_bf16():
+    """bf16 activations and h (the W4A16 variant): x decoded by torch's bfloat16 view, the
+    weights dequantised by np.repeat, SwiGLU by torch, h rounded by the separately pinned
+    bf16 rounding; the oracle must agree to fp64 summation order (a skipped rounding of h
+    moves y by ~1e-4)."""
+    inp = synth.make_inputs("decode256_w4a16_shared", S=1, T_s=6, H=256, I=256, E=1, k=1, shared_I=0)
+    xb = np.asarray(inp.x).reshape(6, 256)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    w13 = codecs.e2m1_unpack(inp.w13[0]) * np.repeat(np.ldexp(1.0, inp.s13[0].astype(int) - 127), 32, 1)
+    w2 = codecs.e2m1_unpack(inp.w2[0]) * np.repeat(np.ldexp(1.0, inp.s2[0].astype(int) - 127), 32, 1)
+    t13, t2 = torch.from_numpy(w13), torch.from_numpy(w2)
+    h = (F.silu(x @ t13[:256].T) * (x @ t13[256:].T)).numpy()
+    ref = torch.from_numpy(codecs.bf16_round(h)) @ t2.T
+    y, hq, hs = layer.expert_ffn(codecs.bf16_decode(xb),
+                                 layer.dequant_weight("fp4", inp.w13[0], inp.s13[0]),
+                                 layer.dequant_weight("fp4", inp.w2[0], inp.s2[0]), 256, "bf16")
+    assert hs is None and np.array_equal(hq, codecs.bf16_round(h))
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * np.abs(ref.numpy()).max())
+    # and the whole layer (E = 1, k = 1, weight 1) returns bf16(y)
+    inp.topk_w[:] = 1.0
+    res = layer.moe_layer(inp)
+    got, want = res["out"].reshape(6, 256), codecs.bf16_round(ref.numpy())
+    # equal but for a rounding flip now and then (fp64 summation order): one ulp at most
+    assert np.mean(got == want) >= 0.99
+    assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(want))
+
+
 def _torch_requant(h):
     """Independent fp32 requantisation with torch float32 ops and torch's e4m3 cast."""
     t = torch.from_numpy(h).to(torch.float32)

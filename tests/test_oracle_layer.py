@@ -2,8 +2,8 @@
 
 The layer is checked against a per-token brute force written here on its own
 (no dispatch at all: out[t] = sum_j w_j FFN_{e_j}(x_t) with dequantisation by
-np.repeat, SwiGLU by torch silu and the 1x128 requantisation by torch float32
-ops), against the identity-expert case (combine returns the dispatched rows
+np.repeat, SwiGLU by torch silu, the 1x128 requantisation by torch float32 ops,
+bf16 activations decoded and h rounded by torch's bfloat16 casts), against the identity-expert case (combine returns the dispatched rows
 bit for bit) and against closed forms of the weighted sum.
 """
 import numpy as np
@@ -40,6 +40,8 @@ def _ffn_brute(fmt, act, x, w13, s13, w2, s2, inter):
     h = (F.silu(tx @ W13[:inter].T) * (tx @ W13[inter:].T)).numpy()
     if act == "fp8":
         h = _requant_torch(h)
+    elif act == "bf16":
+        h = torch.from_numpy(h).to(torch.bfloat16).to(torch.float64).numpy()
     return (torch.from_numpy(h) @ W2.T).numpy()[0]
 
 
@@ -56,6 +58,8 @@ def brute_force(inp):
         for t in range(T_s):
             if inp.act == "fp8":
                 x = codecs.e4m3_decode(inp.x[s, t]) * np.repeat(inp.x_scale[s, t], 128)
+            elif inp.act == "bf16":
+                x = torch.from_numpy(inp.x[s, t].view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
             else:
                 x = inp.x[s, t].astype(np.float64)
             acc = np.zeros(H)
@@ -78,6 +82,7 @@ TINY = [
     ("tiny_f32", dict(T_s=6)),
     ("decode128_fp8", dict(S=3, T_s=4, H=256, I=384, E=5, k=3)),
     ("decode256_mxfp4_shared", dict(S=2, T_s=3, H=256, I=256, E=4, k=2, shared_I=128)),
+    ("decode256_w4a16_shared", dict(S=2, T_s=3, H=256, I=256, E=4, k=2, shared_I=128)),
     ("prefill4096_zipf_fp8", dict(S=2, T_s=5, H=128, I=256, E=6, k=4)),
 ]
 

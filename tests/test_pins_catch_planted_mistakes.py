@@ -52,6 +52,9 @@ MISTAKES = [
      "np.asarray(x, dtype=np.float64) @ np.asarray(wr, dtype=np.float64).T * (1 + 1e-9)"),   # router
     ("codecs.py", "b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16",
      "b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15"),          # bf16 decode
+    ("layer.py", "        h_used = hq\n", "        h_used = h\n"),              # W4A16: h not rounded
+    ("layer.py", "        return codecs.bf16_decode(x.reshape(S * T_s, H))",
+     "        return codecs.bf16_decode(x.reshape(S * T_s, H)) * (1 + 2.0 ** -10)"),  # W4A16: x
 ]
 
 
