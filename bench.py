@@ -72,9 +72,12 @@ def algorithmic_bytes(inp, cnt):
         w2 = H * I // 2 + H * I // 32
         w13_sh = 2 * Ish * H // 2 + 2 * Ish * H // 32
         w2_sh = H * Ish // 2 + H * Ish // 32
-    xrow = H + (H // 128) * 4
-    hrow = I + (I // 128) * 4
-    hrow_sh = Ish + (Ish // 128) * 4 if Ish else 0
+    if inp.act == "bf16":  # W4A16: x and h rows are bf16, no scales
+        xrow, hrow, hrow_sh = 2 * H, 2 * I, 2 * Ish
+    else:
+        xrow = H + (H // 128) * 4
+        hrow = I + (I // 128) * 4
+        hrow_sh = Ish + (Ish // 128) * 4 if Ish else 0
     d = {}
     # dispatch: ids read, each source row read once, R window rows (+scales) written, control state
     d["dispatch"] = T * k * 4 + T * xrow + R * xrow + T * k * 4 + S * T_s * k * 4 + 2 * S * E * 4
@@ -176,8 +179,12 @@ def _cpu_once(inp, n_experts):
     rows = layer.expert_rows(route["cnt"], route["off"], inp.T_s, inp.k)
     t1 = time.perf_counter()
     x = np.asarray(inp.x).reshape(inp.S * inp.T_s, inp.H)
-    xs = np.asarray(inp.x_scale).reshape(inp.S * inp.T_s, inp.H // 128)
-    xt = layer.dequant_act_fp8(x, xs)
+    if inp.act == "bf16":
+        from oracle import codecs
+        xt = codecs.bf16_decode(x)
+    else:
+        xs = np.asarray(inp.x_scale).reshape(inp.S * inp.T_s, inp.H // 128)
+        xt = layer.dequant_act_fp8(x, xs)
     R = inp.S * inp.T_s * inp.k
     y = np.zeros((R, inp.H))
     src = np.where(route["row_src"] >= 0, route["row_src"] // inp.k, -1)
@@ -186,7 +193,7 @@ def _cpu_once(inp, n_experts):
         r = rows[e]
         w13 = layer.dequant_weight(inp.weight, inp.w13[e], inp.s13[e])
         w2 = layer.dequant_weight(inp.weight, inp.w2[e], inp.s2[e])
-        ye, _, _ = layer.expert_ffn(xt[src[r]], w13, w2, inp.I, True)
+        ye, _, _ = layer.expert_ffn(xt[src[r]], w13, w2, inp.I, layer.h_format(inp.act))
         y[r] = layer.round_out(ye, inp.out)
     t2 = time.perf_counter()
     layer.combine(y, route["dst_row"], inp.topk_w)
@@ -264,7 +271,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if inp.act == "fp8" else "f32",
+        "dtype": {"fp8": "fp8", "bf16": "bf16"}.get(inp.act, "f32"),
         "data": "synthetic",
         "config": {"workload": args.workload, "sources": inp.S, "tokens_per_source": inp.T_s,
                    "tokens": inp.S * inp.T_s, "hidden": inp.H, "inter": inp.I, "experts": inp.E,

@@ -191,7 +191,12 @@ class DeviceInputs:
 
     def __init__(self, inp, device="cuda"):
         def up(a):
-            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:  # bf16 bit patterns
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
         self.inp = inp
         self.x = [up(inp.x[s]) for s in range(inp.S)]
         self.x_scale = [up(inp.x_scale[s]) for s in range(inp.S)] if inp.x_scale is not None else None

@@ -42,6 +42,7 @@ struct moe_ctx {
   int device = 0;
   int64_t R_cap = 0, rows_cap = 0;
   int hstride = 0;  // elements per h row = max(I, Ish)
+  int act_bytes = 0;  // bytes per activation (and h) element: 1 FP8, 2 bf16, 4 fp32
   int row_bytes = 0;
   // workspace
   uint8_t* win = nullptr;
@@ -116,10 +117,11 @@ moe_status check_config(const moe_config* c) {
   const bool fp8 = c->act == MOE_FP8_E4M3 && (c->weight == MOE_FP8_E4M3 || c->weight == MOE_FP4_E2M1) &&
                    c->out == MOE_BF16;
   const bool f32 = c->act == MOE_F32 && c->weight == MOE_F32 && c->out == MOE_F32;
-  if (!fp8 && !f32)
+  const bool w4a16 = c->act == MOE_BF16 && c->weight == MOE_FP4_E2M1 && c->out == MOE_BF16;
+  if (!fp8 && !f32 && !w4a16)
     return fail(MOE_ERR_INVALID_ARG,
-                "dtype combination act=%d weight=%d out=%d is not one of (fp8, fp8|fp4, bf16) or "
-                "(f32, f32, f32)",
+                "dtype combination act=%d weight=%d out=%d is not one of (fp8, fp8|fp4, bf16), "
+                "(bf16, fp4, bf16) or (f32, f32, f32)",
                 c->act, c->weight, c->out);
   if (c->sched != MOE_SCHED_FENCE && c->sched != MOE_SCHED_SENTINEL)
     return fail(MOE_ERR_INVALID_ARG, "unknown schedule %d", c->sched);
@@ -176,20 +178,21 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   };
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) return cleanup(fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e)));
-  const bool f32 = cfg->act == MOE_F32;
+  const bool f32 = cfg->act == MOE_F32, fp8 = cfg->act == MOE_FP8_E4M3;
   const int S = cfg->n_src, Tc = cfg->max_tokens, k = cfg->topk, E = cfg->n_experts, H = cfg->hidden;
   c->R_cap = (int64_t)S * Tc * k;
   c->rows_cap = c->R_cap + (int64_t)S * Tc;
   c->hstride = std::max(cfg->inter, cfg->shared_inter);
-  c->row_bytes = f32 ? 4 * H : H;
+  c->act_bytes = f32 ? 4 : fp8 ? 1 : 2;
+  c->row_bytes = c->act_bytes * H;
   const size_t one = 1;
   auto alloc = [&](void** p, size_t bytes) {
     return hipMalloc(p, std::max(bytes, one));
   };
   if ((e = alloc((void**)&c->win, (size_t)c->R_cap * c->row_bytes)) != hipSuccess ||
-      (e = alloc((void**)&c->wsc, f32 ? 0 : (size_t)c->R_cap * (H / 128) * 4)) != hipSuccess ||
-      (e = alloc((void**)&c->h, (size_t)c->rows_cap * c->hstride * (f32 ? 4 : 1))) != hipSuccess ||
-      (e = alloc((void**)&c->hs, f32 ? 0 : (size_t)c->rows_cap * (c->hstride / 128) * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->wsc, fp8 ? (size_t)c->R_cap * (H / 128) * 4 : 0)) != hipSuccess ||
+      (e = alloc((void**)&c->h, (size_t)c->rows_cap * c->hstride * c->act_bytes)) != hipSuccess ||
+      (e = alloc((void**)&c->hs, fp8 ? (size_t)c->rows_cap * (c->hstride / 128) * 4 : 0)) != hipSuccess ||
       (e = alloc(&c->y, (size_t)c->rows_cap * H * (f32 ? 4 : 2))) != hipSuccess ||
       (e = alloc((void**)&c->cnt, (size_t)S * E * 4)) != hipSuccess ||
       (e = alloc((void**)&c->off, (size_t)S * E * 4)) != hipSuccess ||
@@ -330,7 +333,8 @@ static bool use_tiled(const moe_ctx* c, const BatchDims& d) {
 // SENTINEL overlaps dispatch with the decode GEMM1 (weight-streaming kernels, two
 // launches); the tiled prefill, fp32 and persistent paths run in stream order.
 static bool sentinel_applies(const moe_ctx* c, int T_s) {
-  if (c->cfg.sched != MOE_SCHED_SENTINEL || c->cfg.act == MOE_F32 || c->opt_persistent || T_s <= 0) return false;
+  const bool persistent = c->opt_persistent && c->cfg.act != MOE_BF16;  // W4A16 always runs two kernels
+  if (c->cfg.sched != MOE_SCHED_SENTINEL || c->cfg.act == MOE_F32 || persistent || T_s <= 0) return false;
   return !use_tiled(c, dims(c, T_s));
 }
 
@@ -342,7 +346,9 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   const moe_config& cf = c->cfg;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
-  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1;
+  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1, a16 = cf.act == MOE_BF16;
+  // the kernel variant: FP8 or MXFP4 weights with FP8 activations, or W4A16
+  const int wf = a16 ? kFmtW4A16 : cf.weight;
   if (!w->w13 || !w->w2 || (!f32 && (!w->s13 || !w->s2)))
     return fail(MOE_ERR_INVALID_ARG, "routed expert weight or scale pointer is NULL");
   if (!aligned16(w->w13) || !aligned16(w->w2)) return fail(MOE_ERR_INVALID_ARG, "weights not 16-byte aligned");
@@ -386,7 +392,8 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.as = c->wsc;
   g.h = c->h;
   g.hs = c->hs;
-  const int nt = tok_tiles(d, c->opt_tiles, fp4);
+  // W4A16 with row-major weights: at most 4 token tiles (5 spill registers)
+  const int nt = a16 && !packed ? std::min(4, tok_tiles(d, c->opt_tiles, fp4)) : tok_tiles(d, c->opt_tiles, fp4);
   // the shared expert (all T rows): chunks of at most one pass each, as separate work items
   g.sh_chunk_rows = 16 * nt;
   g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
@@ -399,17 +406,17 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     g1.epoch = c->opt_stall ? c->epoch ^ 0x80000000u : c->epoch;  // stall: an epoch never published
     g1.spin_limit = c->spin_limit;
     if (fused) {
-      HIP_TRY(launch_gemm1_lowp(g1, cf.weight, packed, nt, stream, fused));
+      HIP_TRY(launch_gemm1_lowp(g1, wf, packed, nt, stream, fused));
       if (timed) record(c, 2, stream);
     } else {
-      HIP_TRY(launch_gemm1_lowp(g1, cf.weight, packed, nt, c->s_comp));
+      HIP_TRY(launch_gemm1_lowp(g1, wf, packed, nt, c->s_comp));
       if (timed) record(c, 2, c->s_comp);
       HIP_TRY(hipEventRecord(c->ev_g1, c->s_comp));
       HIP_TRY(hipStreamWaitEvent(stream, c->ev_disp, 0));
       HIP_TRY(hipStreamWaitEvent(stream, c->ev_g1, 0));
     }
-  } else if (!tiled && (f32 || !c->opt_persistent)) {
-    HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, cf.weight, packed, nt, stream));
+  } else if (!tiled && (f32 || a16 || !c->opt_persistent)) {
+    HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, wf, packed, nt, stream));
     if (timed) record(c, 2, stream);
   }
   // GEMM2
@@ -443,8 +450,8 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     if (timed) record(c, 2, stream);
     return MOE_OK;
   }
-  if (f32 || !c->opt_persistent || sn) {
-    HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, cf.weight, packed, nt, stream));
+  if (f32 || a16 || !c->opt_persistent || sn) {
+    HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, wf, packed, nt, stream));
     return MOE_OK;
   }
   ExpertsArgs ea{};
@@ -546,15 +553,15 @@ moe_status moe_get_routing(moe_ctx* c, int32_t* cnt, int32_t* off, int32_t* dst_
 
 moe_status moe_copy_buffer(moe_ctx* c, moe_buffer which, void* dst, size_t bytes, hipStream_t stream) {
   if (!c || !dst) return fail(MOE_ERR_INVALID_ARG, "ctx or dst is NULL");
-  const bool f32 = c->cfg.act == MOE_F32;
+  const bool f32 = c->cfg.act == MOE_F32, fp8 = c->cfg.act == MOE_FP8_E4M3;
   const int H = c->cfg.hidden;
   const void* src = nullptr;
   size_t cap = 0;
   switch (which) {
     case MOE_BUF_WINDOW: src = c->win; cap = (size_t)c->R_cap * c->row_bytes; break;
-    case MOE_BUF_WSCALE: src = c->wsc; cap = f32 ? 0 : (size_t)c->R_cap * (H / 128) * 4; break;
-    case MOE_BUF_H: src = c->h; cap = (size_t)c->rows_cap * c->hstride * (f32 ? 4 : 1); break;
-    case MOE_BUF_HSCALE: src = c->hs; cap = f32 ? 0 : (size_t)c->rows_cap * (c->hstride / 128) * 4; break;
+    case MOE_BUF_WSCALE: src = c->wsc; cap = fp8 ? (size_t)c->R_cap * (H / 128) * 4 : 0; break;
+    case MOE_BUF_H: src = c->h; cap = (size_t)c->rows_cap * c->hstride * c->act_bytes; break;
+    case MOE_BUF_HSCALE: src = c->hs; cap = fp8 ? (size_t)c->rows_cap * (c->hstride / 128) * 4 : 0; break;
     case MOE_BUF_Y: src = c->y; cap = (size_t)c->rows_cap * H * (f32 ? 4 : 2); break;
     default: return fail(MOE_ERR_INVALID_ARG, "unknown buffer %d", (int)which);
   }

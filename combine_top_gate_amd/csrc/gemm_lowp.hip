@@ -52,20 +52,38 @@ __device__ __forceinline__ float gloadf(const float* p) { return *(const GLOBAL 
 __device__ __forceinline__ uint32_t gload32(const uint8_t* p) { return *(const GLOBAL uint32_t*)p; }
 __device__ __forceinline__ uint32_t gload8(const uint8_t* p) { return *(const GLOBAL uint8_t*)p; }
 
+// A kernel variant: weight storage and the activations' form.  kFmtW4A16 stores MXFP4
+// weights like MOE_FP4_E2M1 but takes bf16 activations and keeps h in bf16.
 template <int WFMT>
 struct WeightFmt;
 template <>
 struct WeightFmt<MOE_FP8_E4M3> {
+  static constexpr int kStore = MOE_FP8_E4M3;
   static constexpr int kLoads = 2;       // 16-byte loads per lane per 16-row tile per K slab
   static constexpr int kSlabBytes = 128; // bytes of one row per K slab
   static constexpr int kMfmaFmt = MFMA_FMT_FP8;
+  static constexpr bool kA16 = false;    // activations (and h) bf16 instead of FP8 + 1x128 scales
 };
 template <>
 struct WeightFmt<MOE_FP4_E2M1> {
+  static constexpr int kStore = MOE_FP4_E2M1;
   static constexpr int kLoads = 1;
   static constexpr int kSlabBytes = 64;
   static constexpr int kMfmaFmt = MFMA_FMT_FP4;
+  static constexpr bool kA16 = false;
 };
+template <>
+struct WeightFmt<kFmtW4A16> {
+  static constexpr int kStore = MOE_FP4_E2M1;
+  static constexpr int kLoads = 1;
+  static constexpr int kSlabBytes = 64;
+  static constexpr int kMfmaFmt = MFMA_FMT_FP4;
+  static constexpr bool kA16 = true;
+};
+template <int WFMT>
+constexpr bool kFp4W = WeightFmt<WFMT>::kStore == MOE_FP4_E2M1;
+template <int WFMT>
+constexpr bool kA16 = WeightFmt<WFMT>::kA16;
 
 // Where one wave's weights (4 tiles of 16 rows) come from.
 template <int WFMT, bool PACKED>
@@ -114,7 +132,7 @@ __device__ __forceinline__ void load_wslab(WSlab<WFMT>& s, const WSrc<WFMT, PACK
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int h = 0; h < WL; ++h) s.w[mt][h] = gload16_nt(p + (mt * WL + h) * 1024);
-    if constexpr (WFMT == MOE_FP4_E2M1) s.e = gload32(ws.ebase + (int64_t)kb * 256);
+    if constexpr (kFp4W<WFMT>) s.e = gload32(ws.ebase + (int64_t)kb * 256);
   } else {
     constexpr int SB = WeightFmt<WFMT>::kSlabBytes;
 #pragma unroll
@@ -123,7 +141,7 @@ __device__ __forceinline__ void load_wslab(WSlab<WFMT>& s, const WSrc<WFMT, PACK
       s.w[mt][0] = gload16_nt(p);
       if constexpr (WL == 2) s.w[mt][1] = gload16_nt(p + 64);
     }
-    if constexpr (WFMT == MOE_FP4_E2M1) {
+    if constexpr (kFp4W<WFMT>) {
       uint32_t e = 0;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) e |= gload8(ws.erow[mt] + kb * 4) << (8 * mt);
@@ -134,38 +152,96 @@ __device__ __forceinline__ void load_wslab(WSlab<WFMT>& s, const WSrc<WFMT, PACK
 
 // A pass's token tiles (16*NT rows) are staged K slab by K slab in LDS, shared by the
 // workgroup's four waves (each wave multiplies the same tokens with its own weight
-// rows).  A staged row takes kTokStride bytes: 128 + 16 of padding, which keeps the
-// B-operand reads (16 rows x 4 lane groups per instruction) free of bank conflicts.
-constexpr int kTokStride = 144;
+// rows).  A staged row takes the slab's bytes (128 FP8, 256 bf16) + 16 of padding: a
+// row stride of 4 (mod 64) dwords keeps the B-operand reads (16 rows of one lane group
+// per 128-bit LDS read cycle) free of bank conflicts.
+template <bool A16>
+struct TokFmt {
+  static constexpr int kRowBytes = A16 ? 256 : 128;  // bytes of one token row per K slab
+  static constexpr int kStride = kRowBytes + 16;      // staged row stride
+  static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per staged row
+  static constexpr int kElem = A16 ? 2 : 1;           // bytes per activation element
+};
 
 // This thread's share of staging one K slab: chunk c = (threadIdx.x + 256 i) mod
-// (16 NT 8) is bytes 16 (c % 8) .. +15 of token row c / 8.  Threads past the last
-// chunk repeat one (same bytes to the same place), so the loads and stores carry no
-// per-thread condition: a divergent branch around them would make the compiler wait
-// for every load in flight, weights included, before the store.
-template <int NT>
+// (16 NT kChunks) is bytes 16 (c % kChunks) .. +15 of token row c / kChunks.  Threads
+// past the last chunk repeat one (same bytes to the same place), so the loads and
+// stores carry no per-thread condition: a divergent branch around them would make the
+// compiler wait for every load in flight, weights included, before the store.
+template <int NT, bool A16>
 struct TokStage {
-  static constexpr int C = (NT * 16 * 8 + 255) / 256;
+  static constexpr int C = (NT * 16 * TokFmt<A16>::kChunks + 255) / 256;
   const uint8_t* src[C];  // the chunk at K slab 0
   int dst[C];             // byte offset in a staging buffer
 };
 
-template <int NT>
-__device__ __forceinline__ void load_tok(u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts, int kb) {
+// One thread's staging registers for one K slab.
+template <int NT, bool A16>
+using TokRegs = u32x4[TokStage<NT, A16>::C];
+
+template <int NT, bool A16>
+__device__ __forceinline__ void load_tok(TokRegs<NT, A16>& tv, const TokStage<NT, A16>& ts, int kb) {
 #pragma unroll
-  for (int i = 0; i < TokStage<NT>::C; ++i) tv[i] = gload16(ts.src[i] + (int64_t)kb * 128);
+  for (int i = 0; i < TokStage<NT, A16>::C; ++i) tv[i] = gload16(ts.src[i] + (int64_t)kb * TokFmt<A16>::kRowBytes);
 }
 
-template <int NT>
-__device__ __forceinline__ void store_tok(uint8_t* buf, const u32x4 (&tv)[TokStage<NT>::C], const TokStage<NT>& ts) {
+template <int NT, bool A16>
+__device__ __forceinline__ void store_tok(uint8_t* buf, const TokRegs<NT, A16>& tv, const TokStage<NT, A16>& ts) {
 #pragma unroll
-  for (int i = 0; i < TokStage<NT>::C; ++i) *reinterpret_cast<u32x4*>(buf + ts.dst[i]) = tv[i];
+  for (int i = 0; i < TokStage<NT, A16>::C; ++i) *reinterpret_cast<u32x4*>(buf + ts.dst[i]) = tv[i];
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// W4A16, one K slab: the weights stay MXFP4 in registers (the FP4 loads above, lane l
+// holding k = 32g..32g+31 of row l%16 and that block's e8m0 scale) and are decoded to
+// bf16 with the scale applied (v_cvt_scalef32_pk_bf16_fp4, exact: an e2m1 value times a
+// power of two), 8 k at a time, for v_mfma_f32_16x16x32_bf16 (lane l: row/column l%16,
+// k = 8g..8g+7 of its 32).  MFMA c of the slab pairs instruction k-slot (g, i) with
+// k = 32g + 8c + i on both sides, so the token fragment is bytes 64g + 16c .. +15 of the
+// staged bf16 row.  The accumulator chains through the slab's four MFMAs; no promotion.
+template <int NT>
+__device__ __forceinline__ void compute_slab_a16(v4f (&acc)[4][NT], const u32x4 (&w)[4], uint32_t e8,
+                                                 const uint8_t* tb) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  float scl[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint32_t e = (e8 >> (8 * mt)) & 0xFFu;
+    scl[mt] = __uint_as_float(e ? e << 23 : 0x00400000u);  // 2^(e - 127); e = 0 is 2^-127
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    bf16x8 av[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t wd = c == 0 ? w[mt].x : c == 1 ? w[mt].y : c == 2 ? w[mt].z : w[mt].w;
+      const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[mt], 0);
+      const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[mt], 1);
+      const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[mt], 2);
+      const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[mt], 3);
+      av[mt] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(tb + (nt * 16 + r16) * TokFmt<true>::kStride + 64 * g4 + 16 * c);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, t);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
+    }
+  }
 }
 
 // MFMAs of one slab: weights from registers, token fragments from the staged slab tb.
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws,
                                              const float* s_tsc, int kb, const uint8_t* tb) {
+  if constexpr (kA16<WFMT>) {
+    const u32x4 w[4] = {s.w[0][0], s.w[1][0], s.w[2][0], s.w[3][0]};
+    compute_slab_a16<NT>(acc, w, s.e, tb);
+    return;
+  }
   float fs[2] = {1.f, 1.f};
   if constexpr (WFMT == MOE_FP8_E4M3) {
     fs[0] = lane_value(ws.fsv[0], kb);
@@ -174,7 +250,7 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint8_t* tr = tb + (nt * 16 + r16) * kTokStride + 16 * g4;
+    const uint8_t* tr = tb + (nt * 16 + r16) * TokFmt<false>::kStride + 16 * g4;
     const u32x4 t0 = *reinterpret_cast<const u32x4*>(tr);
     const u32x4 t1 = *reinterpret_cast<const u32x4*>(tr + 64);
     const v8i bv = {(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
@@ -186,7 +262,7 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT
                  (int)s.w[mt][1].x, (int)s.w[mt][1].y, (int)s.w[mt][1].z, (int)s.w[mt][1].w};
       else
         av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w, 0, 0, 0, 0};
-      const int ea = WFMT == MOE_FP4_E2M1 ? (int)((s.e >> (8 * mt)) & 0xFFu) : E8M0_ONE;
+      const int ea = kFp4W<WFMT> ? (int)((s.e >> (8 * mt)) & 0xFFu) : E8M0_ONE;
       const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           av, bv, v4f{0.f, 0.f, 0.f, 0.f}, WeightFmt<WFMT>::kMfmaFmt, MFMA_FMT_FP8, 0, ea, 0, E8M0_ONE);
       const float sc = (WFMT == MOE_FP8_E4M3 ? fs[ws.fsel[mt]] : 1.f) * s_tsc[kb * (16 * NT) + nt * 16 + r16];
@@ -208,25 +284,27 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT
 // leaves the weights in flight.  s_tsc holds the pass's token scales, [kb][16*NT].
 // On entry w0 holds (in flight) the weights of slab 0.
 template <int WFMT, bool PACKED, int NT>
-__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws, const TokStage<NT>& ts,
-                                         uint8_t* s_tok, const float* s_tsc, int KB, WSlab<WFMT>& w0) {
-  constexpr int BUF = 16 * NT * kTokStride;
+__device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws,
+                                         const TokStage<NT, kA16<WFMT>>& ts, uint8_t* s_tok, const float* s_tsc, int KB,
+                                         WSlab<WFMT>& w0) {
+  constexpr bool A16 = kA16<WFMT>;
+  constexpr int BUF = 16 * NT * TokFmt<A16>::kStride;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-  u32x4 tv[TokStage<NT>::C];
-  load_tok<NT>(tv, ts, 0);
-  store_tok<NT>(s_tok, tv, ts);
+  TokRegs<NT, A16> tv;
+  load_tok<NT, A16>(tv, ts, 0);
+  store_tok<NT, A16>(s_tok, tv, ts);
   __syncthreads();
   // one K step: `next` receives the weights of slab kb + 1
   auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& next) {
-    if (kb + 1 < KB) load_tok<NT>(tv, ts, kb + 1);
+    if (kb + 1 < KB) load_tok<NT, A16>(tv, ts, kb + 1);
     if (kb + 1 < KB) load_wslab(next, ws, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute_slab<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, s_tok + (kb & 1) * BUF);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < KB) store_tok<NT>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
+    if (kb + 1 < KB) store_tok<NT, A16>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
     __syncthreads();
   };
   WSlab<WFMT> w1;
@@ -240,12 +318,15 @@ constexpr int kMaxKB = MOE_MAX_DIM / 128;  // K slabs (the weight-scale lanes ho
 constexpr int kMaxTok = 6 * 16;            // tokens per pass
 
 // Dynamic LDS of the decode GEMM kernels, sized per launch for K slabs and at most
-// NTMAX token tiles per pass: the pass's token scales [KB][16*NT] fp32, then the two
-// token staging buffers: a few tens of KB instead of the worst case.
+// NTMAX token tiles per pass: the pass's token scales [KB][16*NT] fp32 (none for bf16
+// activations), then the two token staging buffers: a few tens of KB instead of the
+// worst case.
 extern __shared__ __align__(16) uint8_t g_lds[];
-__host__ __device__ constexpr int lds_tsc_bytes(int KB, int ntmax) { return (KB * 16 * ntmax * 4 + 15) / 16 * 16; }
-__host__ __device__ constexpr int lds_bytes(int KB, int ntmax) {
-  return lds_tsc_bytes(KB, ntmax) + 2 * 16 * ntmax * kTokStride;
+__host__ __device__ constexpr int lds_tsc_bytes(int KB, int ntmax, bool a16 = false) {
+  return a16 ? 0 : (KB * 16 * ntmax * 4 + 15) / 16 * 16;
+}
+__host__ __device__ constexpr int lds_bytes(int KB, int ntmax, bool a16 = false) {
+  return lds_tsc_bytes(KB, ntmax, a16) + 2 * 16 * ntmax * (a16 ? TokFmt<true>::kStride : TokFmt<false>::kStride);
 }
 
 // The pass's token scales into LDS, s_tsc[kb][nt*16 + r16] = scale of this lane's token
@@ -341,30 +422,32 @@ __device__ __forceinline__ bool sentinel_wait(const GemmArgs& p, const uint32_t*
   return ok;
 }
 
-// Where token row mm of group g lives: its bytes (K slab 0), its scale row, and the
-// h / y row its result goes to.
-template <bool GEMM1>
+// Where token row mm of group g lives: its bytes (K slab 0), its scale row (none for
+// bf16 activations), and the h / y row its result goes to.
+template <bool GEMM1, bool A16>
 __device__ __forceinline__ void token_row(const GemmArgs& p, const SegTable& t, int g, int mm, const uint8_t*& row,
                                           const float*& sc, int& r) {
   const BatchDims& d = p.d;
   const bool shared = g == d.E;
+  constexpr int EB = TokFmt<A16>::kElem;
+  sc = nullptr;
   if (GEMM1 && shared) {
     const int s = mm / d.T_s, tt = mm - s * d.T_s;
-    row = p.src.x[s] + (int64_t)tt * d.H;
-    sc = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
+    row = p.src.x[s] + (int64_t)tt * d.H * EB;
+    if constexpr (!A16) sc = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
     r = d.R + mm;
   } else {
     r = shared ? d.R + mm : seg_row(t, d.S, mm);
     const int stride = GEMM1 ? d.H : d.hstride;
-    row = p.a + (int64_t)r * stride;
-    sc = p.as + (int64_t)r * (stride >> 7);
+    row = p.a + (int64_t)r * stride * EB;
+    if constexpr (!A16) sc = p.as + (int64_t)r * (stride >> 7);
   }
 }
 
 // Token rows of one pass for this lane (column r16 of each 16-token tile): scales and
 // output rows (-1 past the expert's end).  Rows past the end read the pass's first
 // row (their results are not stored).
-template <int NT, bool GEMM1>
+template <int NT, bool GEMM1, bool A16>
 __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
                                           const float* (&tsc)[NT], int (&orow)[NT]) {
   const int r16 = threadIdx.x & 15;
@@ -373,25 +456,27 @@ __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, 
     const int m = m0 + nt * 16 + r16;
     const uint8_t* row;
     int r;
-    token_row<GEMM1>(p, t, g, m < M ? m : m0, row, tsc[nt], r);
+    token_row<GEMM1, A16>(p, t, g, m < M ? m : m0, row, tsc[nt], r);
     orow[nt] = m < M ? r : -1;
   }
 }
 
 // This thread's chunks of the pass's token staging (TokStage).
-template <int NT, bool GEMM1>
+template <int NT, bool GEMM1, bool A16>
 __device__ __forceinline__ void stage_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
-                                           TokStage<NT>& ts) {
+                                           TokStage<NT, A16>& ts) {
+  constexpr int CH = TokFmt<A16>::kChunks;
 #pragma unroll
-  for (int i = 0; i < TokStage<NT>::C; ++i) {
-    const int c = (threadIdx.x + 256 * i) % (16 * NT * 8), row = c >> 3;
-    ts.dst[i] = row * kTokStride + 16 * (c & 7);
+  for (int i = 0; i < TokStage<NT, A16>::C; ++i) {
+    const unsigned c = (threadIdx.x + 256u * i) % (16u * NT * CH);
+    const int row = (int)(c / CH);
+    ts.dst[i] = row * TokFmt<A16>::kStride + 16 * (int)(c % CH);
     const int m = m0 + row;
     const uint8_t* rp;
     const float* sc;
     int r;
-    token_row<GEMM1>(p, t, g, m < M ? m : m0, rp, sc, r);
-    ts.src[i] = rp + 16 * (c & 7);
+    token_row<GEMM1, A16>(p, t, g, m < M ? m : m0, rp, sc, r);
+    ts.src[i] = rp + 16 * (int)(c % CH);
   }
 }
 
@@ -404,19 +489,40 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const int KB = d.H >> 7;
+  constexpr bool A16 = kA16<WFMT>;
   const float* tsc[NT];
   int orow[NT];
-  TokStage<NT> ts;
+  TokStage<NT, A16> ts;
   WSlab<WFMT> w0;
   load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, true>(p, t, g, M, m0, tsc, orow);
-  stage_rows<NT, true>(p, t, g, M, m0, ts);
-  stage_token_scales<NT>(s_tsc, tsc, KB);
+  pass_rows<NT, true, A16>(p, t, g, M, m0, tsc, orow);
+  stage_rows<NT, true, A16>(p, t, g, M, m0, ts);
+  if constexpr (!A16) stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
   mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
 
+  if constexpr (A16) {
+    // SwiGLU, h stored bf16: this lane holds rows rb + 16t + 4*g4 + i of token column
+    // nt*16 + r16, i.e. 4 consecutive h elements of that token's row
+    const int rb = nb * 128 + 32 * wave;
+    uint16_t* hb = reinterpret_cast<uint16_t*>(p.h);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (orow[nt] < 0) continue;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = silu(acc[t][nt][i]) * acc[2 + t][nt][i];
+        *reinterpret_cast<uint2*>(hb + (int64_t)orow[nt] * d.hstride + rb + 16 * t + 4 * g4) =
+            make_uint2(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
+      }
+    }
+    __syncthreads();  // the token staging buffers are reused by the next pass
+    return;
+  }
   // SwiGLU; this lane holds rows rb + 16t + 4*g4 + i (t = 0, 1) of token column nt*16 + r16
   float hv[2][NT][4];
 #pragma unroll
@@ -483,14 +589,15 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
   if (M == 0) return;  // no rows: no weight traffic (uniform over the workgroup)
 
   const int K = d.H, KB = K >> 7;
-  constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
+  constexpr bool FP4 = kFp4W<WFMT>;
+  constexpr int SF = WeightFmt<WFMT>::kStore;
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
   const uint8_t* WSb = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) +
                        (shared ? 0 : (int64_t)g * p.ws_stride * (FP4 ? 1 : 4));
   WSrc<WFMT, PACKED> ws;
   const int rb = nb * 128 + 32 * wave;  // this wave's gate rows rb..rb+31; up rows inter + same
   if constexpr (PACKED) {
-    ws.base = W + pack_w13_offset(WFMT, K, nb, wave, 0) + 16 * lane;
+    ws.base = W + pack_w13_offset(SF, K, nb, wave, 0) + 16 * lane;
     if constexpr (FP4) ws.ebase = WSb + pack_e13_offset(K, nb, wave, 0) + 4 * lane;
   } else {
     const int64_t wrow = FP4 ? (K >> 1) : K;
@@ -533,7 +640,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs 
   __shared__ float s_amax[4][kMaxTok];
   __shared__ SegTable seg;
   float* s_tsc = reinterpret_cast<float*>(g_lds);
-  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.H >> 7, NTMAX);
+  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.H >> 7, NTMAX, kA16<WFMT>);
   if ((int)blockIdx.x < ndisp) {
     // the launch sizes the dynamic LDS to hold a DispatchSmem as well
     const int b = blockIdx.x;
@@ -553,15 +660,16 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
   const int KB = K >> 7;
+  constexpr bool A16 = kA16<WFMT>;
   const float* tsc[NT];
   int orow[NT];
-  TokStage<NT> ts;
+  TokStage<NT, A16> ts;
   WSlab<WFMT> w0;
   load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, false>(p, t, g, M, m0, tsc, orow);
-  stage_rows<NT, false>(p, t, g, M, m0, ts);
-  stage_token_scales<NT>(s_tsc, tsc, KB);
+  pass_rows<NT, false, A16>(p, t, g, M, m0, tsc, orow);
+  stage_rows<NT, false, A16>(p, t, g, M, m0, ts);
+  if constexpr (!A16) stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
   // a wave past a ragged end of H repeats the last tile's rows and stores nothing
@@ -604,13 +712,14 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
   const int mb = g == d.E ? chunk * p.sh_chunk_rows : 0;
   const int me = g == d.E ? min(M, mb + p.sh_chunk_rows) : M;
 
-  constexpr bool FP4 = WFMT == MOE_FP4_E2M1;
+  constexpr bool FP4 = kFp4W<WFMT>;
+  constexpr int SF = WeightFmt<WFMT>::kStore;
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
   const uint8_t* WSb = static_cast<const uint8_t*>(shared ? p.ws_sh : p.ws) +
                        (shared ? 0 : (int64_t)g * p.ws_stride * (FP4 ? 1 : 4));
   WSrc<WFMT, PACKED> ws;
   if constexpr (PACKED) {
-    ws.base = W + pack_w2_offset(WFMT, K, nb, wave, 0) + 16 * lane;
+    ws.base = W + pack_w2_offset(SF, K, nb, wave, 0) + 16 * lane;
     if constexpr (FP4) ws.ebase = WSb + pack_e2_offset(K, nb, wave, 0) + 4 * lane;
   } else {
     const int64_t wrow = FP4 ? (K >> 1) : K;
@@ -646,7 +755,7 @@ template <int NTMAX, int WFMT, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   __shared__ SegTable seg;
   float* s_tsc = reinterpret_cast<float*>(g_lds);
-  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.hstride >> 7, NTMAX);
+  uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.hstride >> 7, NTMAX, kA16<WFMT>);
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
   int g, nb;
   work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, blockIdx.x, g, nb);
@@ -749,17 +858,18 @@ hipError_t launch1(const GemmArgs& a, int nt, const DispatchArgs* fused, hipStre
   const dim3 grid(ndisp + a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
   const int KB = a.d.H >> 7;
   auto lds = [&](int ntmax) {
-    const int b = lds_bytes(KB, ntmax);
+    const int b = lds_bytes(KB, ntmax, kA16<WFMT>);
     return (size_t)(ndisp && b < (int)sizeof(DispatchSmem) ? (int)sizeof(DispatchSmem) : b);
   };
   if (nt <= 2)
     hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, lds(2), st, a, da, ndisp, chunks);
   else if (nt == 3)
     hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, lds(3), st, a, da, ndisp, chunks);
-  else if (nt == 4 || WFMT != MOE_FP4_E2M1)
+  else if (nt == 4 || !kFp4W<WFMT>)
     hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, lds(4), st, a, da, ndisp, chunks);
   else
-    hipLaunchKernelGGL((k_gemm1_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, lds(5), st, a, da, ndisp, chunks);
+    hipLaunchKernelGGL((k_gemm1_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED>), grid, block, lds(5), st, a, da,
+                       ndisp, chunks);
   return hipGetLastError();
 }
 
@@ -768,14 +878,16 @@ hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   const int nbh = (a.d.H + 255) >> 8;
   const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh * a.sh_chunks : 0)), block(256);
   const int KB = a.d.hstride >> 7;
+  constexpr bool A16 = kA16<WFMT>;
   if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, lds_bytes(KB, 2), st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, lds_bytes(KB, 2, A16), st, a);
   else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, lds_bytes(KB, 3), st, a);
-  else if (nt == 4 || WFMT != MOE_FP4_E2M1)
-    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, lds_bytes(KB, 4), st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, lds_bytes(KB, 3, A16), st, a);
+  else if (nt == 4 || !kFp4W<WFMT>)
+    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, lds_bytes(KB, 4, A16), st, a);
   else
-    hipLaunchKernelGGL((k_gemm2_lowp<5, MOE_FP4_E2M1, PACKED>), grid, block, lds_bytes(KB, 5), st, a);
+    hipLaunchKernelGGL((k_gemm2_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED>), grid, block,
+                       lds_bytes(KB, 5, A16), st, a);
   return hipGetLastError();
 }
 
@@ -825,6 +937,8 @@ int experts_lowp_blocks_per_cu(int weight_fmt, int packed, int tok_tiles, int k_
 
 hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st,
                              const DispatchArgs* fused) {
+  if (weight_fmt == kFmtW4A16)
+    return packed ? launch1<kFmtW4A16, true>(a, tok_tiles, fused, st) : launch1<kFmtW4A16, false>(a, tok_tiles, fused, st);
   if (weight_fmt == MOE_FP4_E2M1)
     return packed ? launch1<MOE_FP4_E2M1, true>(a, tok_tiles, fused, st)
                   : launch1<MOE_FP4_E2M1, false>(a, tok_tiles, fused, st);
@@ -833,6 +947,8 @@ hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int 
 }
 
 hipError_t launch_gemm2_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st) {
+  if (weight_fmt == kFmtW4A16)
+    return packed ? launch2<kFmtW4A16, true>(a, tok_tiles, st) : launch2<kFmtW4A16, false>(a, tok_tiles, st);
   if (weight_fmt == MOE_FP4_E2M1)
     return packed ? launch2<MOE_FP4_E2M1, true>(a, tok_tiles, st) : launch2<MOE_FP4_E2M1, false>(a, tok_tiles, st);
   return packed ? launch2<MOE_FP8_E4M3, true>(a, tok_tiles, st) : launch2<MOE_FP8_E4M3, false>(a, tok_tiles, st);

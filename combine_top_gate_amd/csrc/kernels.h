@@ -64,7 +64,10 @@ struct GemmArgs {
   uint32_t epoch;
   uint32_t spin_limit;
 };
-// weight_fmt: MOE_FP8_E4M3 or MOE_FP4_E2M1; packed: weights in the pack_layout.h order;
+// The W4A16 variant of the decode GEMMs: MXFP4 weights (stored as MOE_FP4_E2M1), bf16
+// activations and bf16 h.  Passed as weight_fmt; not a moe_dtype.
+constexpr int kFmtW4A16 = 16;
+// weight_fmt: MOE_FP8_E4M3, MOE_FP4_E2M1 or kFmtW4A16; packed: weights in the pack_layout.h order;
 // tok_tiles: most 16-token tiles per pass (2..4)
 // fused: also run these dispatch chunks in the launch's first workgroups (SENTINEL)
 hipError_t launch_gemm1_lowp(const GemmArgs& a, int weight_fmt, int packed, int tok_tiles, hipStream_t st,

@@ -113,9 +113,11 @@ typedef struct moe_config {
   int32_t n_experts;      /* E local routed experts, 1..MOE_MAX_EXPERTS */
   int32_t topk;           /* k, 1..MOE_MAX_TOPK */
   int32_t shared_inter;   /* I of the one shared expert, multiple of 128; 0 = none */
-  moe_dtype act;          /* MOE_FP8_E4M3 (with 1x128 scales) or MOE_F32 */
-  moe_dtype weight;       /* MOE_FP8_E4M3 or MOE_FP4_E2M1 (with MOE_FP8_E4M3 act), or MOE_F32 */
-  moe_dtype out;          /* MOE_BF16 (FP8 act) or MOE_F32 (F32 act) */
+  moe_dtype act;          /* MOE_FP8_E4M3 (with 1x128 scales), MOE_BF16 (the W4A16 variant:
+                             MXFP4 weights, bf16 activations and h) or MOE_F32 */
+  moe_dtype weight;       /* MOE_FP8_E4M3 or MOE_FP4_E2M1 (with MOE_FP8_E4M3 act), MOE_FP4_E2M1
+                             (with MOE_BF16 act), or MOE_F32 */
+  moe_dtype out;          /* MOE_BF16 (FP8 or BF16 act) or MOE_F32 (F32 act) */
   moe_schedule sched;     /* FENCE or SENTINEL */
   int32_t dispatch_cus;   /* SENTINEL: 0 = dispatch inside the GEMM1 launch; else the
                              CUs of a separate dispatch stream, a multiple of 8 (the
@@ -145,9 +147,9 @@ typedef struct moe_ctx moe_ctx;
 
 /* Internal buffers that moe_copy_buffer can read (parity tests of intermediate steps). */
 typedef enum {
-  MOE_BUF_WINDOW = 0,   /* dispatched rows: [R][H] bytes (FP8) or [R][H] f32, R = S*T_s*k */
+  MOE_BUF_WINDOW = 0,   /* dispatched rows: [R][H] in the activation dtype (e4m3, bf16 or f32), R = S*T_s*k */
   MOE_BUF_WSCALE = 1,   /* their scales: f32 [R][H/128] (FP8 act only) */
-  MOE_BUF_H = 2,        /* SwiGLU output: FP8 [R + T][I] (or f32 for F32 act); rows R.. = shared expert */
+  MOE_BUF_H = 2,        /* SwiGLU output [R + T][max(I, shared_I)] in the activation dtype; rows R.. = shared expert */
   MOE_BUF_HSCALE = 3,   /* its 1x128 scales: f32 [R + T][I/128] (FP8 act only) */
   MOE_BUF_Y = 4         /* expert outputs: [R + T][H] in the output dtype; rows R.. = shared expert */
 } moe_buffer;
@@ -162,10 +164,10 @@ moe_status moe_destroy(moe_ctx* ctx);
 /*
  * Dispatch [S sources x T_s tokens x k slots] into the windows.
  *   tokens_per_src  T_s, 0..max_tokens (0 = nothing to do)
- *   x               host array [S] of device pointers; x[s] -> [T_s][H] e4m3 bytes
- *                   (or f32 for F32 act), 16-byte aligned
+ *   x               host array [S] of device pointers; x[s] -> [T_s][H] in the activation
+ *                   dtype (e4m3 bytes, bf16 or f32), 16-byte aligned
  *   x_scale         host array [S] of device pointers; x_scale[s] -> f32 [T_s][H/128]
- *                   (FP8 act); NULL for F32 act
+ *                   (FP8 act); NULL for BF16 and F32 act
  *   ids             device int32 [S][T_s][k]: local expert id of each slot, -1 = not
  *                   routed to this GPU; ids outside [-1, E) set MOE_DEVERR_BAD_ID and
  *                   the pair is dropped
@@ -226,7 +228,8 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *   MOE_OPT_PERSISTENT_GEMM  0: two kernels, one workgroup per work item (default);
  *                            1: both GEMMs in one persistent kernel fed by work queues,
  *                            GEMM2 items waiting on per-expert counters (the cross-XCD
- *                            hand-off of h costs an L2 write-back per item).
+ *                            hand-off of h costs an L2 write-back per item).  The W4A16
+ *                            variant always runs two kernels.
  *   MOE_OPT_TOKEN_TILES      0: automatic; 2..6: most 16-row token tiles per GEMM pass
  *                            (kernels take at most 4 for FP8 and 5 for MXFP4 weights).
  *   MOE_OPT_QUEUE            0: automatic; 1: one work queue per XCD (an expert's items

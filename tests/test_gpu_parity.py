@@ -250,6 +250,65 @@ def check_fp8_outputs(inp, ref, g, out):
     assert close_rows(out.reshape(T, -1), np.asarray(ref["out"]).reshape(T, -1), tol, allow_out, allow_out_el)
 
 
+def bf16_h_check(x_rows, w13, inter, g_h):
+    """W4A16: the GPU's bf16 h against the oracle's exact SwiGLU value, elementwise:
+    |g - h| <= band + 2^-8 (|h| + band).  band bounds the GPU's value before rounding:
+    Higham's gamma_n (n = H + 16) times the sum of |terms| of the gate and up dot products,
+    carried through SwiGLU, plus gamma_n |h|.  Rounding that value to bf16 (8 significant
+    bits, to nearest) moves it by at most 2^-8 of its magnitude.
+    Returns the largest |g - h| / bound."""
+    H = x_rows.shape[1]
+    n = H + 16
+    gam = n * U32 / (1 - n * U32)
+    a = x_rows @ w13.T
+    mag = np.abs(x_rows) @ np.abs(w13).T
+    g, u = a[:, :inter], a[:, inter:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sg
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    h = silu * u
+    band = gam * (np.abs(dsilu * u) * mag[:, :inter] + np.abs(silu) * mag[:, inter:] + np.abs(h))
+    bound = band + 2.0 ** -8 * (np.abs(h) + band) + 1e-30
+    r = np.abs(g_h - h) / bound
+    assert np.all(r <= 1.0), f"h outside its bound by {r.max():.3f}"
+    return float(r.max())
+
+
+def check_w4a16(inp, ref, g, out):
+    """W4A16: h of every used window row and shared row within bf16_h_check's bound; y
+    rows and the combined output to the FP8 criterion (no requantisation step here, so
+    no allowance is needed)."""
+    T, R, tol = inp.S * inp.T_s, inp.S * inp.T_s * inp.k, TOL[inp.out]
+    xt = codecs.bf16_decode(np.asarray(inp.x).reshape(T, inp.H))
+    worst = 0.0
+    for e, r in enumerate(ref["expert_rows"]):
+        if len(r):
+            w13 = layer.dequant_weight(inp.weight, inp.w13[e], inp.s13[e])
+            worst = max(worst, bf16_h_check(xt[ref["row_src"][r] // inp.k], w13, inp.I, g["h"][r, :inp.I]))
+    if inp.shared_I:
+        w13 = layer.dequant_weight(inp.weight, inp.sh_w13, inp.sh_s13)
+        worst = max(worst, bf16_h_check(xt, w13, inp.shared_I, g["h"][R:R + T, :inp.shared_I]))
+    print(f"  h: largest |g - h| / bound {worst:.3f}", flush=True)
+    used = ref["row_src"] >= 0
+    assert close(g["y"][:R][used], ref["y_win"][used], tol)
+    if inp.shared_I:
+        assert close(g["y"][R:R + T], ref["y_shared"], tol)
+    assert close(out.reshape(T, -1), np.asarray(ref["out"]).reshape(T, -1), tol)
+    # regression guard: with every activation bf16 the error is a few bf16 roundings, not an
+    # e4m3 step; each output row within one bf16 rounding (2^-8) of the oracle's
+    r = np.asarray(ref["out"]).reshape(T, -1)
+    num = np.linalg.norm(out.reshape(T, -1) - r, axis=1)
+    den = np.maximum(np.linalg.norm(r, axis=1), 1e-30)
+    assert np.all(num <= 2.0 ** -8 * den), float(np.max(num / den))
+
+
+def check_outputs(inp, ref, g, out):
+    if inp.act == "bf16":
+        check_w4a16(inp, ref, g, out)
+    else:
+        check_fp8_outputs(inp, ref, g, out)
+
+
 def close_rows(gy, ry, tol, allow, allow_el=None):
     """Per-row relative L2 <= tol after the allowance, plus the elementwise guard; the
     fraction of elements above tol is counted over the rows with no allowance (a row that
@@ -315,6 +374,12 @@ def gpu_state(moe, inp):
             np.float32).reshape(R + T, hstride // 128)
         y = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 2)
         st["y"] = bf16_np(y.view(torch.int16)).reshape(R + T, H)
+    elif inp.act == "bf16":
+        st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H * 2).cpu().numpy().view(np.uint16).reshape(R, H)
+        h = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride * 2)
+        st["h"] = bf16_np(h.view(torch.int16)).reshape(R + T, hstride)
+        y = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 2)
+        st["y"] = bf16_np(y.view(torch.int16)).reshape(R + T, H)
     else:
         st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H * 4).cpu().numpy().view(np.float32).reshape(R, H)
         st["h"] = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride * 4).cpu().numpy().view(
@@ -344,6 +409,12 @@ SMALL = [
     ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=12), True),
     ("prefill4096_zipf_fp8", dict(S=2, T_s=40, H=256, I=384, E=6, k=4, seed=13), True),
     ("decode128_fp8", dict(S=5, T_s=3, H=128, I=128, E=7, k=2, seed=14), True),
+    # W4A16: bf16 activations and h, MXFP4 weights; ragged passes, k = 1, one pass of 5 tiles
+    ("decode256_w4a16_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=18), False),
+    ("decode256_w4a16_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=18), True),
+    ("decode256_w4a16_shared", dict(S=3, T_s=4, H=256, I=128, E=6, k=1, shared_I=128, seed=19), True),
+    ("decode256_w4a16_shared", dict(S=4, T_s=20, H=512, I=384, E=3, k=3, shared_I=0, seed=20), True),
+    ("decode256_w4a16_shared", dict(S=4, T_s=20, H=512, I=384, E=3, k=3, shared_I=0, seed=20), False),
 ]
 
 
@@ -372,14 +443,14 @@ def test_stages_match_oracle(name, over, packed):
         gh = layer.dequant_act_fp8(hq, g["hs"][:R, :inp.I // 128][used])
         rh = layer.dequant_act_fp8(rq, ref["h_scales"][used])
         assert np.linalg.norm(gh - rh) <= 1e-2 * np.linalg.norm(rh)
-    else:
+    elif inp.act == "f32":
         assert rel_err(g["h"][:R, :inp.I][used], _f32_h(inp, ref)[used]) <= 1e-4
     tol = TOL[inp.out]
     if inp.act == "f32":
         assert rel_err(g["y"][:R][used], ref["y_win"][used]) <= tol
         assert rel_err(out_np(inp, d.out), ref["out"]) <= tol
     else:
-        check_fp8_outputs(inp, ref, g, out_np(inp, d.out))
+        check_outputs(inp, ref, g, out_np(inp, d.out))
     assert moe.device_error() == 0
 
 
@@ -408,7 +479,7 @@ def _full(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "decode128_fp8", "decode8_fp8", "decode256_mxfp4_shared",
-                                  "prefill4096_zipf_fp8"])
+                                  "prefill4096_zipf_fp8", "decode256_w4a16_shared"])
 def test_full_size(name):
     inp = _full(name)
     moe, d = run(inp, packed=inp.weight != "f32")
@@ -440,6 +511,7 @@ def test_full_size(name):
 @pytest.mark.parametrize("name,over", [
     ("decode128_fp8", dict(S=4, T_s=9, H=512, I=384, E=6, k=3, seed=51)),
     ("decode256_mxfp4_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=52)),
+    ("decode256_w4a16_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=56)),
     ("decode128_fp8", {}),
 ])
 def test_packed_weights_give_identical_output(name, over):
@@ -525,6 +597,8 @@ SENTINEL_CASES = [
     ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=72), 0),
     ("decode128_fp8", dict(S=8, T_s=5, H=256, I=128, E=16, k=4, seed=73), 8),
     ("decode128_fp8", dict(S=4, T_s=3, H=256, I=256, E=6, k=2, seed=74), 32),
+    ("decode256_w4a16_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=75), 0),
+    ("decode256_w4a16_shared", dict(S=4, T_s=6, H=256, I=256, E=6, k=2, shared_I=0, seed=76), 16),
 ]
 
 
@@ -699,6 +773,8 @@ MAXCASES = [
     ("decode128_fp8", dict(S=32, T_s=2, H=128, I=128, E=256, k=16, seed=44), False),
     ("tiny_f32", dict(S=1, T_s=4, H=16384, I=256, E=2, k=1, seed=45), False),
     ("prefill4096_zipf_fp8", dict(S=2, T_s=192, H=16384, I=256, E=2, k=1, seed=46), True),
+    ("decode256_w4a16_shared", dict(S=2, T_s=3, H=16384, I=128, E=2, k=1, shared_I=256, seed=47), True),
+    ("decode256_w4a16_shared", dict(S=2, T_s=3, H=128, I=16384, E=2, k=2, shared_I=0, seed=48), False),
 ]
 
 
@@ -712,5 +788,5 @@ def test_maximum_sizes(name, over, packed):
     if inp.act == "f32":
         assert rel_err(out_np(inp, d.out), ref["out"]) <= TOL["f32"]
     else:
-        check_fp8_outputs(inp, ref, g, out_np(inp, d.out))
+        check_outputs(inp, ref, g, out_np(inp, d.out))
     assert moe.device_error() == 0
