@@ -274,6 +274,18 @@ def combine(y_win, dst_row, topk_w, y_shared=None):
     return out
 
 
+def combine_fp8(y_win, dst_row, topk_w, y_shared=None):
+    """The combined output requantised as the next layer's FP8 input: the sums of
+    combine() (exact, before any output rounding), then the 1x128 rule of requant_1x128
+    along each token row.  Reading taken for the requantisation the pages fuse into the
+    layer [GC-MoE feed, Full text]: applied to the layer's output as well, by the same
+    rule as to h.  Returns (codes uint8 [S][T_s][H], scales fp64 [S][T_s][H/128])."""
+    out = combine(y_win, dst_row, topk_w, y_shared)
+    S, T_s, H = out.shape
+    q, s = requant_1x128(out.reshape(S * T_s, H))
+    return q.reshape(S, T_s, H), s.reshape(S, T_s, H // BLOCK)
+
+
 # --------------------------------------------------------------------------
 # whole layer
 # --------------------------------------------------------------------------

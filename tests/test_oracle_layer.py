@@ -172,3 +172,48 @@ def test_empty_and_unrouted():
     inp.ids[:] = -1
     res = layer.moe_layer(inp)
     assert np.all(res["out"] == 0) and res["cnt"].sum() == 0
+
+
+def test_fp8_output_round_trips_representable_rows():
+    """k = 1, weight 1, no shared expert: y rows that are e4m3 values times 2^-5 (448 in
+    every block) come back as their own codes and scale, block by block."""
+    rng = np.random.default_rng(21)
+    S, T_s, H = 2, 3, 384
+    codes = rng.integers(0, 0x7E, (S * T_s, H)).astype(np.uint8) | (rng.integers(0, 2, (S * T_s, H)) << 7).astype(np.uint8)
+    codes[:, ::128] = 0x7E                   # +448 at the start of every block
+    y = codecs.e4m3_decode(codes) * 2.0 ** -5
+    dst = np.arange(S * T_s, dtype=np.int32).reshape(S, T_s, 1)
+    w = np.ones((S, T_s, 1), np.float32)
+    q, sc = layer.combine_fp8(y, dst, w)
+    assert np.all(sc == 2.0 ** -5)
+    nz = (codes & 0x7F) != 0
+    assert np.array_equal(q.reshape(S * T_s, H)[nz], codes[nz])
+    assert np.all((q.reshape(S * T_s, H)[~nz] & 0x7F) == 0)
+
+
+def test_fp8_output_matches_torch():
+    """Random rows, k = 3 with an unrouted slot and a shared expert: the fp64 weighted sums
+    in slot order (written here), then torch float32 ops and torch's e4m3 cast."""
+    rng = np.random.default_rng(22)
+    S, T_s, k, H, R = 2, 4, 3, 256, 24
+    y = rng.standard_normal((R, H)) * 10 ** rng.uniform(-2, 2, (R, 1))
+    ysh = rng.standard_normal((S * T_s, H))
+    dst = rng.permutation(R)[:S * T_s * k].reshape(S, T_s, k).astype(np.int32)
+    dst[1, 2, 1] = -1
+    w = rng.uniform(0, 1, (S, T_s, k)).astype(np.float32)
+    acc = np.zeros((S * T_s, H))
+    for s in range(S):
+        for t in range(T_s):
+            for j in range(k):
+                if dst[s, t, j] >= 0:
+                    acc[s * T_s + t] += float(w[s, t, j]) * y[dst[s, t, j]]
+            acc[s * T_s + t] += ysh[s * T_s + t]
+    tt = torch.from_numpy(acc).to(torch.float32).reshape(S * T_s, H // 128, 128)
+    amax = tt.abs().amax(dim=2)
+    sc = torch.where(amax > 0, amax / torch.tensor(448.0), torch.ones_like(amax))
+    rq = torch.clamp(tt / sc[:, :, None], -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    q, s_ = layer.combine_fp8(y, dst, w, ysh)
+    assert np.array_equal(s_.reshape(S * T_s, -1), sc.to(torch.float64).numpy())
+    rq = rq.reshape(S * T_s, H).numpy()
+    nz = (rq & 0x7F) != 0
+    assert np.array_equal(q.reshape(S * T_s, H)[nz], rq[nz])

@@ -55,6 +55,10 @@ MISTAKES = [
     ("layer.py", "        h_used = hq\n", "        h_used = h\n"),              # W4A16: h not rounded
     ("layer.py", "        return codecs.bf16_decode(x.reshape(S * T_s, H))",
      "        return codecs.bf16_decode(x.reshape(S * T_s, H)) * (1 + 2.0 ** -10)"),  # W4A16: x
+    ("layer.py", "    q, s = requant_1x128(out.reshape(S * T_s, H))",
+     "    q, s = requant_1x128(codecs.bf16_round(out).reshape(S * T_s, H))"),     # FP8 out from bf16
+    ("layer.py", "    return q.reshape(S, T_s, H), s.reshape(S, T_s, H // BLOCK)",
+     "    return q.reshape(S, T_s, H), s.reshape(S, H // BLOCK, T_s).transpose(0, 2, 1)"),  # scales
 ]
 
 
