@@ -108,6 +108,29 @@ def read_traffic():
 GATE_EXPERTS = 256  # the router scores every global expert (DeepSeek-V3 shape)
 
 
+def time_combine_fp8(torch, moe, d, inp, nbytes_combine, calls=200):
+    """Microseconds per FP8-output combine (the layer's output requantised 1x128 for the
+    next layer) on the last layer's expert outputs, timed like the gate; its bytes are the
+    plain combine's with the token rows written as e4m3 codes + scales instead of bf16."""
+    T, H = inp.S * inp.T_s, inp.H
+    q = torch.empty((inp.S, inp.T_s, H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((inp.S, inp.T_s, H // 128), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        moe.combine_fp8(d.topk_w, q, sc)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(50_000_000)
+    e0.record()
+    for _ in range(calls):
+        moe.combine_fp8(d.topk_w, q, sc)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    nbytes = nbytes_combine - T * H * 2 + T * H + T * (H // 128) * 4
+    return {"us_per_call": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes,
+            "method": f"{calls} back-to-back calls queued behind a GPU spin, HIP events"}
+
+
 def time_gate(torch, binding, synth, T, H, k, calls=200):
     """Microseconds per fused gate call (router + top-k softmax) for T tokens.
 
@@ -298,6 +321,9 @@ def main():
     mfma = measure_fp8_mfma(torch, binding)
     rec["fp8_mfma_measured_TFLOPs"] = mfma
     rec["fractions"]["gemm_of_measured_fp8_mfma"] = round(rec["gemm_TFLOPs"] / mfma, 4)
+    if inp.out == "bf16":
+        print("[bench] FP8-output combine timing", file=sys.stderr, flush=True)
+        rec["combine_fp8_out"] = time_combine_fp8(torch, moe, d, inp, nbytes["combine"])
     if not args.no_gate:
         print("[bench] gate timing", file=sys.stderr, flush=True)
         rec["gate_us"] = time_gate(torch, binding, synth, inp.S * inp.T_s, inp.H, inp.k)

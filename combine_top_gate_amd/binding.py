@@ -77,6 +77,7 @@ def load():
         "moe_dispatch": (st, [VP, I32, P(VP), P(VP), VP, VP]),
         "moe_grouped_gemm": (st, [VP, P(MoeWeights), VP]),
         "moe_combine": (st, [VP, VP, VP, VP]),
+        "moe_combine_fp8": (st, [VP, VP, VP, VP, VP]),
         "moe_layer": (st, [VP, I32, P(VP), P(VP), VP, VP, P(MoeWeights), VP, VP]),
         "moe_get_routing": (st, [VP, VP, VP, VP, VP, VP]),
         "moe_copy_buffer": (st, [VP, ctypes.c_int, VP, ctypes.c_size_t, VP]),
@@ -254,6 +255,11 @@ class Moe:
 
     def combine(self, topk_w, out):
         _check(self.lib.moe_combine(self.ctx, _ptr(topk_w), _ptr(out), _stream()))
+
+    def combine_fp8(self, topk_w, out, out_scale):
+        """The combine with its output requantised to e4m3 codes (uint8 [S][T_s][H]) and
+        1x128 fp32 scales ([S][T_s][H/128])."""
+        _check(self.lib.moe_combine_fp8(self.ctx, _ptr(topk_w), _ptr(out), _ptr(out_scale), _stream()))
 
     def layer(self, T_s, x, x_scale, ids, topk_w, weights, out):
         xa, sa = self._ptr_array(x), self._ptr_array(x_scale)

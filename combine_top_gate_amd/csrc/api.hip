@@ -488,7 +488,21 @@ moe_status moe_combine(moe_ctx* c, const float* topk_w, void* out, hipStream_t s
   if (!aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "out is not 16-byte aligned");
   const moe_config& cf = c->cfg;
   const BatchDims d = dims(c);
-  CombineArgs a{c->dst_row, topk_w, c->y, out, d.T, d.k, d.H, d.R, cf.shared_inter > 0, cf.out == MOE_F32};
+  CombineArgs a{c->dst_row, topk_w, c->y, out, d.T, d.k, d.H, d.R, cf.shared_inter > 0, cf.out == MOE_F32, nullptr};
+  HIP_TRY(launch_combine(a, stream));
+  return MOE_OK;
+}
+
+moe_status moe_combine_fp8(moe_ctx* c, const float* topk_w, uint8_t* out, float* out_scale, hipStream_t stream) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
+  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine_fp8 before any moe_dispatch");
+  if (c->T_s == 0) return MOE_OK;
+  if (!topk_w || !out || !out_scale) return fail(MOE_ERR_INVALID_ARG, "topk_w, out or out_scale is NULL");
+  if (!aligned16(out) || ((uintptr_t)out_scale & 3u))
+    return fail(MOE_ERR_INVALID_ARG, "out is not 16-byte aligned or out_scale not 4-byte aligned");
+  const moe_config& cf = c->cfg;
+  const BatchDims d = dims(c);
+  CombineArgs a{c->dst_row, topk_w, c->y, out, d.T, d.k, d.H, d.R, cf.shared_inter > 0, cf.out == MOE_F32, out_scale};
   HIP_TRY(launch_combine(a, stream));
   return MOE_OK;
 }

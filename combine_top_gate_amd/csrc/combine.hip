@@ -4,6 +4,7 @@
 // ("Relay Buffer Independent Communication over Pooled HBM for Efficient MoE
 // Inference on Ascend", abstract: direct reading from expert windows).
 // Each thread owns one 16-byte piece of a token row: 8 bf16 or 4 fp32 values.  k <= 16.
+// The output is the row in y's dtype, or FP8 codes with 1x128 scales for the next layer.
 #include "kernels.h"
 
 namespace {
@@ -11,7 +12,13 @@ namespace {
 // KM >= k row slots are loaded (a slot past k, or with no row, loads row 0 and is not
 // added), so the loads carry no condition and are all in flight together; then the rows
 // are added in slot order, the shared expert's (weight 1) last.
-template <bool F32, int KM, bool SH>
+//
+// Q8: the output is requantised for the next layer's FP8 input instead of rounded to
+// the output dtype: per token row and 128-element block, s = fl32(amax / 448) (1 when
+// amax = 0) and code = e4m3(clamp(fl32(v / s), +-448)), nearest even -- the rule of the
+// h requantisation.  A block is 128 / V consecutive threads (aligned, all active since
+// H is a multiple of 128), so its amax is a butterfly over those lanes.
+template <bool F32, int KM, bool SH, bool Q8>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   constexpr int V = F32 ? 4 : 8;
   const int tok = blockIdx.x;
@@ -58,7 +65,25 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   for (int j = 0; j < KM; ++j)
     if (rows[j] >= 0) add(yv[j], wts[j]);  // uniform
   if constexpr (SH) add(ysh, 1.0f);
-  if constexpr (F32) {
+  if constexpr (Q8) {
+    constexpr int L = 128 / V;  // lanes per block
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) m = fmaxf(m, fabsf(acc[v]));
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float sc = m > 0.f ? m / 448.0f : 1.0f;
+    float q[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) q[v] = fminf(fmaxf(acc[v] / sc, -448.0f), 448.0f);
+    uint8_t* orow = static_cast<uint8_t*>(a.out) + (int64_t)tok * a.H + c;
+    if constexpr (F32) {
+      *reinterpret_cast<uint32_t*>(orow) = pack4_e4m3(q[0], q[1], q[2], q[3]);
+    } else {
+      *reinterpret_cast<uint2*>(orow) = make_uint2(pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7]));
+    }
+    if ((threadIdx.x & (L - 1)) == 0) a.out_scale[(int64_t)tok * (a.H >> 7) + (c >> 7)] = sc;
+  } else if constexpr (F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (int64_t)tok * a.H + c) =
         make_float4(acc[0], acc[1], acc[2], acc[3]);
   } else {
@@ -71,26 +96,32 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
 }
 
-template <bool F32, bool SH>
+template <bool F32, bool SH, bool Q8>
 void launch_km(const CombineArgs& a, dim3 grid, hipStream_t st) {
   if (a.k <= 2)
-    hipLaunchKernelGGL((k_combine<F32, 2, SH>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_combine<F32, 2, SH, Q8>), grid, dim3(256), 0, st, a);
   else if (a.k <= 4)
-    hipLaunchKernelGGL((k_combine<F32, 4, SH>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_combine<F32, 4, SH, Q8>), grid, dim3(256), 0, st, a);
   else if (a.k <= 8)
-    hipLaunchKernelGGL((k_combine<F32, 8, SH>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_combine<F32, 8, SH, Q8>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_combine<F32, MOE_MAX_TOPK, SH>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_combine<F32, MOE_MAX_TOPK, SH, Q8>), grid, dim3(256), 0, st, a);
+}
+
+template <bool F32, bool Q8>
+void launch_sh(const CombineArgs& a, dim3 grid, hipStream_t st) {
+  a.has_shared ? launch_km<F32, true, Q8>(a, grid, st) : launch_km<F32, false, Q8>(a, grid, st);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  const int V = a.out_f32 ? 4 : 8;
+  const int V = a.y_f32 ? 4 : 8;
   const dim3 grid(a.T, (a.H + 256 * V - 1) / (256 * V));
-  if (a.out_f32)
-    a.has_shared ? launch_km<true, true>(a, grid, st) : launch_km<true, false>(a, grid, st);
+  const bool q8 = a.out_scale != nullptr;
+  if (a.y_f32)
+    q8 ? launch_sh<true, true>(a, grid, st) : launch_sh<true, false>(a, grid, st);
   else
-    a.has_shared ? launch_km<false, true>(a, grid, st) : launch_km<false, false>(a, grid, st);
+    q8 ? launch_sh<false, true>(a, grid, st) : launch_sh<false, false>(a, grid, st);
   return hipGetLastError();
 }

@@ -119,10 +119,11 @@ struct CombineArgs {
   const int32_t* dst_row;  // [S][T_s][k]
   const float* topk_w;     // [S][T_s][k]
   const void* y;           // [R+T][H] bf16 or f32
-  void* out;               // [S][T_s][H]
+  void* out;               // [S][T_s][H] in y's dtype, or e4m3 codes when out_scale is set
   int T, k, H, R;
   int has_shared;
-  int out_f32;
+  int y_f32;               // y (and a plain out) are fp32
+  float* out_scale;        // null: out in y's dtype; else FP8 out, f32 [S][T_s][H/128]
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 

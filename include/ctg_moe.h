@@ -190,6 +190,20 @@ moe_status moe_grouped_gemm(moe_ctx* ctx, const moe_weights* w, hipStream_t stre
  */
 moe_status moe_combine(moe_ctx* ctx, const float* topk_w, void* out, hipStream_t stream);
 
+/*
+ * The same combine with its output requantised as the next layer's FP8 input (the
+ * requantisation the layer fuses [GC-MoE feed, full text], here also applied to the
+ * layer's output): the fp32 slot-order sums of moe_combine, then per token row and
+ * 128-element block s = fl32(amax / 448) (1 when amax = 0) and code = e4m3 of
+ * clamp(fl32(v / s), +-448), nearest even -- the rule of the h requantisation.
+ * Any configuration (y bf16 or fp32).
+ *   out        device u8 [S][T_s][H] e4m3 codes, 16-byte aligned
+ *   out_scale  device f32 [S][T_s][H/128], 4-byte aligned
+ * NULL or misaligned pointers return MOE_ERR_INVALID_ARG; before any dispatch likewise.
+ */
+moe_status moe_combine_fp8(moe_ctx* ctx, const float* topk_w, uint8_t* out, float* out_scale,
+                           hipStream_t stream);
+
 /* The whole layer: dispatch, grouped GEMM and combine, synchronised per cfg.sched. */
 moe_status moe_layer(moe_ctx* ctx, int32_t tokens_per_src, const void* const* x,
                      const float* const* x_scale, const int32_t* ids, const float* topk_w,

@@ -1,0 +1,137 @@
+"""GPU parity of the combine with FP8 output (moe_combine_fp8) through the C-ABI.
+
+Given the GPU's own expert outputs y (read back after the layer ran), the oracle's
+combine_fp8 defines the codes and scales.  The kernel forms each sum with k + 1 fused
+multiply-adds in fp32 in slot order, so it is within gamma_{k+1} * (sum_j |w_j y_j| +
+|y_shared|) of the exact sum (Higham); a code may differ from the oracle's only where
+that band reaches an e4m3 rounding boundary (or moves the block's scale, by the band of
+its amax), and every code is checked to be a rounding of a value inside the band.
+End to end, the dequantised output is compared with the oracle's exact layer output to
+the FP8 criterion after one e4m3 rounding: per row, ||deq - r|| <= (2e-2 + 2^-4) ||r||
+(rounding to e4m3 moves each element by at most 2^-4 of its magnitude).  The bf16
+output of moe_combine from the same sums is within one e4m3 rounding of the codes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_top_gate_amd import binding, synth
+from oracle import codecs, layer
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def bf16_np(t):
+    u = t.contiguous().view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def run_fp8_out(inp, packed):
+    print(f"[gpu case] combine_fp8 {inp.name} S={inp.S} T_s={inp.T_s} H={inp.H} I={inp.I} E={inp.E} "
+          f"k={inp.k} act={inp.act} shared={inp.shared_I} packed={packed}", flush=True)
+    moe = binding.Moe.for_inputs(inp)
+    d = binding.DeviceInputs(inp)
+    if packed:
+        moe.pack(d)
+    moe.run(d)
+    q = torch.empty((inp.S, inp.T_s, inp.H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((inp.S, inp.T_s, inp.H // 128), dtype=torch.float32, device="cuda")
+    moe.combine_fp8(d.topk_w, q, sc)
+    torch.cuda.synchronize()
+    R, T, H = inp.S * inp.T_s * inp.k, inp.S * inp.T_s, inp.H
+    ybytes = (R + T) * H * (4 if inp.out == "f32" else 2)
+    yb = moe.buffer(binding.MOE_BUF_Y, ybytes)
+    y = yb.cpu().numpy().view(np.float32).astype(np.float64) if inp.out == "f32" else bf16_np(yb.view(torch.int16))
+    y = y.reshape(R + T, H)
+    dst = moe.routing(inp.S, inp.T_s, inp.k, inp.E)[2].cpu().numpy()
+    assert moe.device_error() == 0
+    return moe, d, q.cpu().numpy(), sc.cpu().numpy().astype(np.float64), y, dst
+
+
+def check_given_y(inp, q, sc, y, dst):
+    """Codes and scales against the oracle's combine_fp8 of the GPU's own y rows."""
+    S, T_s, k, H = inp.S, inp.T_s, inp.k, inp.H
+    R, T = S * T_s * k, S * T_s
+    ysh = y[R:R + T] if inp.shared_I else None
+    rq, rs = layer.combine_fp8(y[:R], dst, inp.topk_w, ysh)
+    # the exact sums and their fp32 band
+    v = layer.combine(y[:R], dst, inp.topk_w, ysh).reshape(T, H)
+    mag = layer.combine(np.abs(y[:R]), dst, np.abs(inp.topk_w), None if ysh is None else np.abs(ysh)).reshape(T, H)
+    n = k + 1
+    band = n * U32 / (1 - n * U32) * mag
+    rs2 = rs.reshape(T, H // 128)
+    s = np.repeat(rs2, 128, axis=1)
+    # the scale's band: that of the block's largest element
+    blk = np.abs(v).reshape(T, H // 128, 128)
+    am = np.argmax(blk, axis=2)
+    amax = np.take_along_axis(blk, am[..., None], 2)[..., 0]
+    bam = np.take_along_axis(band.reshape(T, H // 128, 128), am[..., None], 2)[..., 0]
+    ds = np.where(amax > 0, bam / np.where(amax > 0, amax, 1.0), 0.0)
+    g_s = sc.reshape(T, H // 128)
+    assert np.all(np.abs(g_s - rs2) <= rs2 * (ds + 4 * U32)), "scale outside its band"
+    x = v / s
+    dx = band / s + np.abs(x) * (np.repeat(ds, 128, axis=1) + 4 * U32)
+    lo = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(x - dx, -448.0, 448.0)))
+    hi = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(x + dx, -448.0, 448.0)))
+    gv = codecs.e4m3_decode(q.reshape(T, H))
+    assert np.all((gv >= lo) & (gv <= hi)), "a code outside the fp32 band"
+    same = (q.reshape(T, H) == rq.reshape(T, H)) | (((q.reshape(T, H) & 0x7F) == 0) & ((rq.reshape(T, H) & 0x7F) == 0))
+    print(f"  codes equal to the oracle's (given y): {same.mean():.6f}; scales equal: "
+          f"{np.mean(g_s == rs2):.6f}", flush=True)
+    assert same.mean() >= 0.999
+    return gv * np.repeat(g_s, 128, axis=1)
+
+
+CASES = [
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=81), True),
+    ("decode128_fp8", dict(S=2, T_s=5, H=256, I=128, E=20, k=16, seed=82), False),
+    ("decode256_mxfp4_shared", dict(S=3, T_s=4, H=256, I=128, E=6, k=1, shared_I=128, seed=83), True),
+    ("decode256_w4a16_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=84), True),
+    ("tiny_f32", dict(E=9, k=5, seed=85), False),
+    ("decode128_fp8", dict(S=2, T_s=3, H=16384, I=128, E=2, k=1, seed=86), True),
+]
+
+
+@pytest.mark.parametrize("name,over,packed", CASES)
+def test_combine_fp8_matches_oracle(name, over, packed):
+    inp = synth.make_inputs(name, **over)
+    moe, d, q, sc, y, dst = run_fp8_out(inp, packed)
+    deq = check_given_y(inp, q, sc, y, dst)
+    T, H = inp.S * inp.T_s, inp.H
+    # end to end against the oracle's exact layer output
+    r = layer.moe_layer(inp)
+    ref = layer.combine(r["y_win"], r["dst_row"], inp.topk_w, r.get("y_shared")).reshape(T, H)
+    tol = 1e-3 if inp.act == "f32" else 2e-2
+    num = np.linalg.norm(deq - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    print(f"  end to end: row relL2 max {np.max(num / den):.3e}", flush=True)
+    assert np.all(num <= (tol + 2.0 ** -4) * den)
+    # the plain combine from the same sums: within one e4m3 rounding of the codes
+    moe.combine(d.topk_w, d.out)
+    torch.cuda.synchronize()
+    plain = (d.out.cpu().numpy().astype(np.float64) if inp.out == "f32" else bf16_np(d.out)).reshape(T, H)
+    assert np.all(np.abs(deq - plain) <= 2.0 ** -4 * np.abs(plain) + 2.0 ** -8 * np.abs(plain)
+                  + 2.0 ** -9 * np.repeat(sc.reshape(T, -1), 128, axis=1))
+
+
+def test_combine_fp8_full_size_decode():
+    inp = synth.make_inputs("decode128_fp8")
+    moe, d, q, sc, y, dst = run_fp8_out(inp, True)
+    check_given_y(inp, q, sc, y, dst)
+
+
+def test_combine_fp8_rejects_bad_arguments():
+    inp = synth.make_inputs("decode128_fp8", S=2, T_s=2, H=256, I=128, E=4, k=2, seed=87)
+    moe = binding.Moe.for_inputs(inp)
+    d = binding.DeviceInputs(inp)
+    moe.run(d)
+    q = torch.empty((2, 2, 256), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((2, 2, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.MoeError, match="NULL"):
+        binding._check(moe.lib.moe_combine_fp8(moe.ctx, binding._ptr(d.topk_w), binding._ptr(q), None,
+                                                binding._stream()))
+    with pytest.raises(binding.MoeError, match="aligned"):
+        binding._check(moe.lib.moe_combine_fp8(moe.ctx, binding._ptr(d.topk_w), binding._ptr(q[0, 0, 1:]),
+                                                binding._ptr(sc), binding._stream()))
