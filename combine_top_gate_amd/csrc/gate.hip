@@ -22,7 +22,7 @@
 // split into ks contiguous slices over workgroups, so that a small batch still spreads
 // over every CU; each workgroup writes its slice's partial tile to a workspace.
 //
-// k_topk: one wave per token, E <= 256 logits, 4 per lane (added up from the ks partial
+// k_topk: one wave (and workgroup) per token, E <= 256 logits, 4 per lane (added up from the ks partial
 // sums in slice order first, when there are several).  The k-th largest logit is
 // found exactly by a radix select over order-preserving 32-bit keys (one ballot per
 // lane register and bit); the k selected logits (ties at the threshold to the lower
@@ -177,13 +177,15 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 
-__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
-  __shared__ uint32_t s_key[4][MOE_MAX_TOPK];
-  __shared__ int s_id[4][MOE_MAX_TOPK];
-  __shared__ float s_val[4][MOE_MAX_TOPK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = min(blockIdx.x * 4 + wave, a.T - 1);  // spare waves redo the last token, not stored
-  const bool store = blockIdx.x * 4 + wave < a.T;
+// One token per 64-thread workgroup: the tokens spread over as many CUs as there are
+// tokens (measured on MI355X against four per workgroup: 17.2 against 18.2 us per gate
+// call at 128 tokens, 10.5 against 11.1 at 8).
+__global__ __launch_bounds__(64) void k_topk(TopkArgs a) {
+  __shared__ uint32_t s_key[MOE_MAX_TOPK];
+  __shared__ int s_id[MOE_MAX_TOPK];
+  __shared__ float s_val[MOE_MAX_TOPK];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
   const float* z = a.logits + (int64_t)t * a.E;
   const int64_t slice_stride = (int64_t)a.T * a.E;
   float v[4];
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
 #pragma unroll
     for (int s = 1; s < kGateMaxSplit; ++s)
       if (s < a.ks) zz += part[j][s];
-    if (e < a.E && a.logits_out && store) a.logits_out[(int64_t)t * a.E + e] = zz;
+    if (e < a.E && a.logits_out) a.logits_out[(int64_t)t * a.E + e] = zz;
     v[j] = e < a.E ? zz : 0.f;
     key[j] = e < a.E ? order_key(zz) : 0u;  // below every real logit's key (k <= E)
   }
@@ -231,31 +233,29 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     const uint64_t msel = __ballot(sel);
     if (sel) {
       const int p = slot + __popcll(msel & below);
-      s_key[wave][p] = key[j];
-      s_id[wave][p] = lane + 64 * j;
-      s_val[wave][p] = v[j];
+      s_key[p] = key[j];
+      s_id[p] = lane + 64 * j;
+      s_val[p] = v[j];
     }
     slot += __popcll(msel);
     eq_left -= min(eq_left, __popcll(meq));
   }
   __syncthreads();
   if (lane < a.k) {
-    const uint32_t mk = s_key[wave][lane];
-    const int mid = s_id[wave][lane];
-    const float mv = s_val[wave][lane];
+    const uint32_t mk = s_key[lane];
+    const int mid = s_id[lane];
+    const float mv = s_val[lane];
     int rank = 0;
     float zmax = -INFINITY;
     for (int p = 0; p < a.k; ++p) {
-      const uint32_t ok = s_key[wave][p];
-      rank += ok > mk || (ok == mk && s_id[wave][p] < mid);
-      zmax = fmaxf(zmax, s_val[wave][p]);
+      const uint32_t ok = s_key[p];
+      rank += ok > mk || (ok == mk && s_id[p] < mid);
+      zmax = fmaxf(zmax, s_val[p]);
     }
     float sum = 0.f;
-    for (int p = 0; p < a.k; ++p) sum += expf(s_val[wave][p] - zmax);
-    if (store) {
-      a.ids[(int64_t)t * a.k + rank] = mid;
-      a.w[(int64_t)t * a.k + rank] = expf(mv - zmax) / sum;
-    }
+    for (int p = 0; p < a.k; ++p) sum += expf(s_val[p] - zmax);
+    a.ids[(int64_t)t * a.k + rank] = mid;
+    a.w[(int64_t)t * a.k + rank] = expf(mv - zmax) / sum;
   }
 }
 
@@ -297,6 +297,6 @@ hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_topk, dim3(a.T), dim3(64), 0, st, a);
   return hipGetLastError();
 }
