@@ -392,7 +392,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.as = c->wsc;
   g.h = c->h;
   g.hs = c->hs;
-  // W4A16 with row-major weights: at most 4 token tiles (5 spill registers)
+  // W4A16 with row-major weights: at most 4 token tiles (with 5 the kernels spill registers)
   const int nt = a16 && !packed ? std::min(4, tok_tiles(d, c->opt_tiles, fp4)) : tok_tiles(d, c->opt_tiles, fp4);
   // the shared expert (all T rows): chunks of at most one pass each, as separate work items
   g.sh_chunk_rows = 16 * nt;

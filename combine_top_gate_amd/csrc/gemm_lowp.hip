@@ -1,9 +1,11 @@
 // Grouped GEMMs over the expert windows, FP8 e4m3 activations x FP8 (128x128 block
 // scales) or MXFP4 (e8m0 1x32 scales) weights, on gfx950 MFMA
-// v_mfma_scale_f32_16x16x128_f8f6f4.
+// v_mfma_scale_f32_16x16x128_f8f6f4; and the W4A16 variant (kFmtW4A16): bf16
+// activations x MXFP4 weights decoded to bf16 in registers, on v_mfma_f32_16x16x32_bf16.
 //
 // GEMM1: a = x W13^T over the window rows of one expert, SwiGLU h = silu(gate) * up,
-//        then h is requantised to e4m3 with one fp32 scale per 128 columns of a row.
+//        then h is requantised to e4m3 with one fp32 scale per 128 columns of a row
+//        (W4A16: h is stored bf16).
 // GEMM2: y = h W2^T, stored bf16.
 // ("GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4 Grouped GEMM via
 // CUDA Green Contexts", full text: block-scaled MMA with operand swap, fused SwiGLU,
