@@ -22,7 +22,7 @@ MOE_SCHED_FENCE, MOE_SCHED_SENTINEL = range(2)
 MOE_BUF_WINDOW, MOE_BUF_WSCALE, MOE_BUF_H, MOE_BUF_HSCALE, MOE_BUF_Y = range(5)
 MOE_DEVERR_BAD_ID, MOE_DEVERR_TIMEOUT = 0x1, 0x2
 (MOE_OPT_PERSISTENT_GEMM, MOE_OPT_TOKEN_TILES, MOE_OPT_QUEUE, MOE_OPT_TILED_GEMM,
- MOE_OPT_SENTINEL_SPIN, MOE_OPT_SENTINEL_STALL) = range(6)
+ MOE_OPT_SENTINEL_SPIN, MOE_OPT_SENTINEL_STALL, MOE_OPT_TILED_MFMA) = range(7)
 
 _DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "fp4": MOE_FP4_E2M1}
 

@@ -68,7 +68,7 @@ struct moe_ctx {
   uint32_t spin_limit = kSentinelSpin;
   int opt_stall = 0;
   // options
-  int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0;
+  int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0, opt_tiled_m32 = 0;
   // state of the last dispatch
   int T_s = -1;
   SrcPtrs src{};
@@ -446,6 +446,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     ta.nb1_s = d.Ish / 128;
     ta.nb2 = (d.H + 255) / 256;
     ta.packed = packed;
+    ta.m32 = c->opt_tiled_m32;
     HIP_TRY(launch_tiled(ta, c->n_cu, stream));
     if (timed) record(c, 2, stream);
     return MOE_OK;
@@ -692,6 +693,10 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
     case MOE_OPT_SENTINEL_STALL:
       if (v != 0 && v != 1) break;
       c->opt_stall = v;
+      return MOE_OK;
+    case MOE_OPT_TILED_MFMA:
+      if (v != 0 && v != 1) break;
+      c->opt_tiled_m32 = v;
       return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);

@@ -176,8 +176,11 @@ __device__ __forceinline__ int seg_row(const Tiles& T, int S, int m) {
   return T.row0[s] + (m - T.pre[s]);
 }
 
-// One item: token tile [m0, m0 + BM) of group g (M rows), weight block nb.
-template <bool GEMM1>
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// One item: token tile [m0, m0 + BM) of group g (M rows), weight block nb.  M32: the K
+// loop on v_mfma_scale_f32_32x32x64_f8f6f4 instead of 16x16x128 (see below).
+template <bool GEMM1, bool M32>
 __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles& T, bool t_packed) {
   const BatchDims& d = p.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -268,13 +271,145 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     dma4(ssrc + kb, sdst);
   };
 
+  const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
+  constexpr int D = kStages - 1;  // slabs in flight ahead of the one multiplied
+  if constexpr (M32) {
+    // 32x32x64 MFMAs.  This wave's 64 weight rows are 2 tiles of 32 (GEMM1: gate rows
+    // wn*32 + r and up rows 128 + wn*32 + r; GEMM2: rows wn*64 + 32 j + r) and its 128
+    // token rows 4 tiles of 32 (wm*128 + 32 tt + r).  Operand lane l holds row (column)
+    // l % 32 and, of the slab's half h (64 k), k = 64 h + 32 (l / 32) + 0..31: the 16-byte
+    // chunks 4 h + 2 (l / 32) and + 1 of its 128-byte row (the same k order on both
+    // sides, so the contraction is right whatever order the instruction sums in).  Result
+    // lane l, register i: weight row 8 (i / 4) + 4 (l / 32) + i % 4 of the tile, token
+    // l % 32 (measured on gfx950).  Per tile and slab the two halves chain in the matrix
+    // core and one promotion follows; the accumulator is still 128 registers per lane,
+    // and the freed result registers let one tile's promotion overlap the next tile's MFMAs.
+    const int r32 = lane & 31, g2 = lane >> 5;
+    // fragment offsets: tiles lie 32 or 128 rows apart (the swizzle term (r >> 1) & 7
+    // unchanged), so each (half, part) is one base plus immediates
+    int aoff[2][2], woff[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        aoff[h][q] = swz(wm * (BM / 2) + r32, 4 * h + 2 * g2 + q);
+        woff[h][q] = t_packed ? wn * 8192 + (r32 >> 4) * 2048 + h * 1024 + ((2 * g2 + q) * 16 + (r32 & 15)) * 16
+                              : swz((GEMM1 ? wn * 32 : wn * 64) + r32, 4 * h + 2 * g2 + q);
+      }
+    const int wstep = t_packed ? 2 * 2048 : (GEMM1 ? 128 : 32) * kStride;  // weight tile j -> j + 1
+    v16f acc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][tt][i] = 0.f;
+    __syncthreads();  // the previous item's last reads of the ring are done
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < KB) issue(i, i);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int st = kb % kStages;
+      if (D > 1 && kb + D - 1 < KB)
+        wait_barrier<(D > 1 ? D - 1 : 0) * kLoadsPerSlab>();
+      else
+        wait_barrier<0>();
+      if (kb + D < KB) issue(kb + D, (kb + D) % kStages);
+      const uint8_t* ws_ = T.w[st];
+      const uint8_t* as_ = T.a[st];
+      v8i wv[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(ws_ + woff[h][0] + j * wstep);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(ws_ + woff[h][1] + j * wstep);
+          wv[j][h] = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+        }
+      const float swj[2] = {T.sw[st][0], T.sw[st][1]};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        v8i bv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 x0 = *reinterpret_cast<const u32x4*>(as_ + aoff[h][0] + tt * 32 * kStride);
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(as_ + aoff[h][1] + tt * 32 * kStride);
+          bv[h] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+        const float sx = T.sx[st][wm * (BM / 2) + 32 * tt + r32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          v16f r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv[j][0], bv[0], v16f{}, MFMA_FMT_FP8, MFMA_FMT_FP8,
+                                                                   0, E8M0_ONE, 0, E8M0_ONE);
+          r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv[j][1], bv[1], r, MFMA_FMT_FP8, MFMA_FMT_FP8, 0,
+                                                              E8M0_ONE, 0, E8M0_ONE);
+          const float sc = swj[GEMM1 ? j : wsel] * sx;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[j][tt][i] = fmaf(r[i], sc, acc[j][tt][i]);
+        }
+      }
+    }
+    // ---- epilogue; lane holds weight rows 8 (i / 4) + 4 g2 + i % 4 of tile j, token
+    // wm*128 + 32 tt + r32
+    if constexpr (GEMM1) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = silu(acc[0][tt][i]) * acc[1][tt][i];
+          acc[0][tt][i] = v;
+          mx = fmaxf(mx, fabsf(v));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (g2 == 0) T.amax[wn][wm * (BM / 2) + 32 * tt + r32] = mx;
+      }
+      __syncthreads();
+      const int hsc_stride = d.hstride >> 7;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int tr = wm * (BM / 2) + 32 * tt + r32;
+        const int m = m0 + tr;
+        if (m >= M) continue;
+        const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+        const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
+        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[0][tt][4 * i4 + i] / sc, -448.0f), 448.0f);
+          *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow * d.hstride + nb * 128 + wn * 32 + 8 * i4 + 4 * g2) =
+              pack4_e4m3(q[0], q[1], q[2], q[3]);
+        }
+        if (wn == 0 && g2 == 0) p.hs[(int64_t)orow * hsc_stride + nb] = sc;
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int m = m0 + wm * (BM / 2) + 32 * tt + r32;
+        if (m >= M) continue;
+        const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int n = nb * BN + wn * 64 + 32 * j + 8 * i4 + 4 * g2;
+            if (n >= d.H) continue;
+            const uint32_t lo = bf16_bits(acc[j][tt][4 * i4]) | (bf16_bits(acc[j][tt][4 * i4 + 1]) << 16);
+            const uint32_t hi = bf16_bits(acc[j][tt][4 * i4 + 2]) | (bf16_bits(acc[j][tt][4 * i4 + 3]) << 16);
+            *reinterpret_cast<uint2*>(p.y + (int64_t)orow * d.H + n) = make_uint2(lo, hi);
+          }
+      }
+    }
+    return;
+  } else {
   // this wave: token tiles wm*(BM/2) + 16*tt (tt < kTT); weight tiles (GEMM1) gate rows
   // wn*32 + 16*j and up rows 128 + wn*32 + 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j
   int wrows[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     wrows[j] = GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
-  const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
   // byte offsets (within a stage) of this lane's fragments
   // Fragment offsets: tiles lie 16 or 128 rows apart, which leaves the swizzle term
   // (r >> 1) & 7 unchanged, so every fragment is a base (two registers per operand)
@@ -293,7 +428,6 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int D = kStages - 1;  // slabs in flight ahead of the one multiplied
   __syncthreads();  // the previous item's last reads of the ring are done
 #pragma unroll
   for (int i = 0; i < D; ++i)
@@ -388,6 +522,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       }
     }
   }
+  }
 }
 
 // Persistent grid: the items of one GEMM from the per-XCD queues.  Queue x holds
@@ -395,7 +530,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
 // Workgroup b runs on XCD b % 8 (the GPU's round-robin placement; any other placement
 // only costs locality).  Slots past an expert's last token tile or column block are
 // empty.  A workgroup leaves when every queue is exhausted.
-template <bool GEMM1>
+template <bool GEMM1, bool M32>
 __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
   __shared__ Tiles T;
   const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
@@ -426,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
     if (tm * BM >= M || nb >= nbg) continue;  // an empty slot (uniform)
     segments(p, g, T);
     __syncthreads();
-    tile_item<GEMM1>(p, g, M, tm * BM, nb, T, t.packed != 0);
+    tile_item<GEMM1, M32>(p, g, M, tm * BM, nb, T, t.packed != 0);
     __syncthreads();
   }
 }
@@ -437,9 +572,15 @@ hipError_t launch_tiled(const TiledArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tiled<true>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (a.m32)
+    hipLaunchKernelGGL((k_tiled<true, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_tiled<true, false>), dim3(grid), dim3(kThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tiled<false>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (a.m32)
+    hipLaunchKernelGGL((k_tiled<false, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_tiled<false, false>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

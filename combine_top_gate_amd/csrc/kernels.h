@@ -93,6 +93,7 @@ struct TiledArgs {
   int nb1_r, nb1_s;    // GEMM1 column blocks (128 gate + 128 up) of a routed / the shared group
   int nb2;             // GEMM2 row blocks of 256
   int packed;          // weights in the pack_layout.h order
+  int m32;             // K loop on 32x32x64 MFMAs (else 16x16x128)
 };
 hipError_t launch_tiled(const TiledArgs& a, int grid, hipStream_t st);
 int tiled_plan_words();

@@ -256,6 +256,10 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *   MOE_OPT_SENTINEL_STALL   1: GEMM1 waits for an epoch the dispatch never publishes,
  *                            so every routed wait times out -- a test of the failure
  *                            path (the layer output is then invalid); 0: off.
+ *   MOE_OPT_TILED_MFMA       the LDS-tiled kernels' MFMA: 0: 16x16x128 (default);
+ *                            1: 32x32x64, the two 64-deep halves of a 128-deep scale block
+ *                            chained before one promotion (results agree with 0 to fp32
+ *                            rounding of the block sums, not bit for bit).
  * Unknown options or values return MOE_ERR_INVALID_ARG.
  */
 typedef enum {
@@ -264,7 +268,8 @@ typedef enum {
   MOE_OPT_QUEUE = 2,
   MOE_OPT_TILED_GEMM = 3,
   MOE_OPT_SENTINEL_SPIN = 4,
-  MOE_OPT_SENTINEL_STALL = 5
+  MOE_OPT_SENTINEL_STALL = 5,
+  MOE_OPT_TILED_MFMA = 6
 } moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 

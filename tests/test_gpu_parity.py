@@ -578,6 +578,57 @@ def test_tiled_gemm_matches_oracle_and_streaming_kernel(name, over, packed):
     assert moe.device_error() == 0
 
 
+@pytest.mark.parametrize("name,over,packed", [
+    ("prefill4096_zipf_fp8", dict(S=4, T_s=96, H=512, I=256, E=8, k=4, seed=61), False),
+    ("prefill4096_zipf_fp8", dict(S=4, T_s=96, H=512, I=256, E=8, k=4, seed=61), True),
+    ("prefill4096_zipf_fp8", dict(S=3, T_s=80, H=384, I=384, E=5, k=3, seed=62), True),
+    ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=63), True),
+])
+def test_tiled_gemm_32x32_matches_oracle(name, over, packed):
+    """The tiled kernels with 32x32x64 MFMAs (MOE_OPT_TILED_MFMA = 1) against the oracle,
+    with the same bars as the 16x16x128 kernels; the two agree up to fp32 rounding of the
+    block sums (codes may differ where that straddles a rounding boundary)."""
+    inp = synth.make_inputs(name, **over)
+    moe = binding.Moe.for_inputs(inp)
+    moe.set_option(binding.MOE_OPT_TILED_GEMM, 1)
+    moe.set_option(binding.MOE_OPT_TILED_MFMA, 1)
+    moe, d = run(inp, moe=moe, packed=packed)
+    ref = layer.moe_layer(inp)
+    g = gpu_state(moe, inp)
+    check_routing(g, ref)
+    used = ref["row_src"] >= 0
+    R = inp.S * inp.T_s * inp.k
+    allow, allow_el = window_allowance(inp, ref, g, used)
+    assert close_rows(g["y"][:R][used], ref["y_win"][used], TOL["bf16"], allow, allow_el)
+    assert close(out_np(inp, d.out), ref["out"], TOL["bf16"])
+    # the 16x16x128 kernels on the same inputs: equal outputs but for those roundings
+    out32 = d.out.clone()
+    moe.set_option(binding.MOE_OPT_TILED_MFMA, 0)
+    moe.run(d)
+    torch.cuda.synchronize()
+    a, b = out_np(inp, out32), out_np(inp, d.out)
+    print(f"  32x32 vs 16x16: {np.mean(a == b):.4f} of outputs equal, max rel "
+          f"{np.max(np.abs(a - b) / np.maximum(np.abs(b), np.sqrt(np.mean(b ** 2)))):.3e}", flush=True)
+    assert moe.device_error() == 0
+
+
+def test_tiled_gemm_32x32_full_size_prefill():
+    inp = _full("prefill4096_zipf_fp8")
+    moe = binding.Moe.for_inputs(inp)
+    moe.set_option(binding.MOE_OPT_TILED_MFMA, 1)
+    moe, d = run(inp, moe=moe, packed=True)
+    rng = np.random.default_rng(1)
+    toks = {(0, 0), (inp.S - 1, inp.T_s - 1)}
+    while len(toks) < 48:
+        toks.add((int(rng.integers(inp.S)), int(rng.integers(inp.T_s))))
+    toks = sorted(toks)
+    want = layer.layer_tokens(inp, toks)
+    got = out_np(inp, d.out)
+    assert close(np.stack([got[s, t] for s, t in toks]), want, TOL["bf16"])
+    assert np.isfinite(got).all()
+    assert moe.device_error() == 0
+
+
 def test_many_back_to_back_calls_reuse_scheduler_state():
     """The persistent GEMM resets its queues and counters itself: 60 calls, no clean pass."""
     inp = synth.make_inputs("decode128_fp8", S=8, T_s=4, H=1024, I=512, E=32, k=4, seed=55)
@@ -678,7 +729,7 @@ def test_invalid_options():
     moe = binding.Moe.for_inputs(inp)
     for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 7), (binding.MOE_OPT_QUEUE, 3),
                      (binding.MOE_OPT_PERSISTENT_GEMM, 2), (binding.MOE_OPT_SENTINEL_SPIN, -1),
-                     (binding.MOE_OPT_SENTINEL_STALL, 2), (9, 0)]:
+                     (binding.MOE_OPT_SENTINEL_STALL, 2), (binding.MOE_OPT_TILED_MFMA, 2), (9, 0)]:
         with pytest.raises(binding.MoeError):
             moe.set_option(opt, val)
 
