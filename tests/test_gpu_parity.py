@@ -532,6 +532,8 @@ def test_packed_weights_give_identical_output(name, over):
     ("decode128_fp8", {}),
     ("decode256_mxfp4_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=53)),
     ("prefill4096_zipf_fp8", dict(S=4, T_s=64, H=512, I=256, E=16, k=4, seed=54)),
+    # W4A16 runs two kernels whatever the persistent option says
+    ("decode256_w4a16_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=57)),
 ])
 def test_gemm_schedules_give_identical_output(name, over):
     """Persistent queues (per XCD or global), separate kernels and any token tiling run
