@@ -179,7 +179,8 @@ __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p))
 
 // One token per 64-thread workgroup: the tokens spread over as many CUs as there are
 // tokens (measured on MI355X against four per workgroup: 17.2 against 18.2 us per gate
-// call at 128 tokens, 10.5 against 11.1 at 8).
+// call at 128 tokens, 10.5 against 11.1 at 8).  NS is a power of two >= ks.
+template <int NS>
 __global__ __launch_bounds__(64) void k_topk(TopkArgs a) {
   __shared__ uint32_t s_key[MOE_MAX_TOPK];
   __shared__ int s_id[MOE_MAX_TOPK];
@@ -190,21 +191,23 @@ __global__ __launch_bounds__(64) void k_topk(TopkArgs a) {
   const int64_t slice_stride = (int64_t)a.T * a.E;
   float v[4];
   uint32_t key[4];
-  // every partial sum's load is issued before the first addition (columns past E read
-  // column E - 1 and are dropped); then the sums are taken in slice order
-  float part[4][kGateMaxSplit];
+  // every partial sum's load is issued before the first addition, with no branch between
+  // them: slices past ks - 1 read slice ks - 1 again and columns past E read column E - 1,
+  // and both are dropped (a load under a per-slice branch made the compiler wait for each
+  // one before issuing the next).  The sums are then taken in slice order.
+  float part[4][NS];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = min(lane + 64 * j, a.E - 1);
 #pragma unroll
-    for (int s = 0; s < kGateMaxSplit; ++s) part[j][s] = s < a.ks ? z[s * slice_stride + e] : 0.f;
+    for (int s = 0; s < NS; ++s) part[j][s] = z[min(s, a.ks - 1) * slice_stride + e];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
     float zz = part[j][0];
 #pragma unroll
-    for (int s = 1; s < kGateMaxSplit; ++s)
+    for (int s = 1; s < NS; ++s)
       if (s < a.ks) zz += part[j][s];
     if (e < a.E && a.logits_out) a.logits_out[(int64_t)t * a.E + e] = zz;
     v[j] = e < a.E ? zz : 0.f;
@@ -274,13 +277,13 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
 
 int gate_split(int T, int H, int E) {
   // Token tiles of up to 128 tokens; split K until about 256 workgroups are in flight, with
-  // at least 8 K steps (two per wave) in every slice.  Up to 64 tokens, at most 8 slices:
-  // the top-k kernel then has half the partial sums to add, and the router's workgroups
-  // are short anyway (measured: 10.6 against 12.4 us at 8 tokens; 16 slices stay better
-  // at 128 tokens, 17.8 against 18.3 us).
+  // at least 8 K steps (two per wave) in every slice.  Measured on MI355X (H 7168, 256
+  // experts, gate call in us), against every fixed split of 1-16: the rule's choice is the
+  // fastest or within 0.1 us of it from 1 to 4096 tokens (e.g. 8.6 at 8 tokens, 11.1 at
+  // 64, 13.6 at 128, 39.3 at 1024).
   const int tiles = ((E + 15) / 16) * ((T + 127) / 128);
   const int ks = (256 + tiles - 1) / tiles;
-  return std::max(1, std::min({ks, T > 64 ? kGateMaxSplit : kGateMaxSplit / 2, H / 256}));
+  return std::max(1, std::min({ks, kGateMaxSplit, H / 256}));
 }
 
 hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st) {
@@ -297,6 +300,16 @@ hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3(a.T), dim3(64), 0, st, a);
+  static_assert(kGateMaxSplit == 16, "k_topk is instantiated for up to 16 slices");
+  if (a.ks <= 1)
+    hipLaunchKernelGGL(k_topk<1>, dim3(a.T), dim3(64), 0, st, a);
+  else if (a.ks <= 2)
+    hipLaunchKernelGGL(k_topk<2>, dim3(a.T), dim3(64), 0, st, a);
+  else if (a.ks <= 4)
+    hipLaunchKernelGGL(k_topk<4>, dim3(a.T), dim3(64), 0, st, a);
+  else if (a.ks <= 8)
+    hipLaunchKernelGGL(k_topk<8>, dim3(a.T), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_topk<16>, dim3(a.T), dim3(64), 0, st, a);
   return hipGetLastError();
 }

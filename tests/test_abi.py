@@ -121,8 +121,13 @@ def test_gate_workspace_sizes(lib):
     assert lib.moe_gate_workspace_bytes(128, 7168, 256) == 16 * 128 * 256 * 4
     # 4096 tokens already give 512 tiles: no split
     assert lib.moe_gate_workspace_bytes(4096, 7168, 256) == 4096 * 256 * 4
+    # a small batch is split 16 ways too
+    assert lib.moe_gate_workspace_bytes(8, 7168, 256) == 16 * 8 * 256 * 4
+    # 512 tokens: 64 tiles, a 4-way split
+    assert lib.moe_gate_workspace_bytes(512, 7168, 256) == 4 * 512 * 256 * 4
     # a short K cannot be split below 8 steps per slice
     assert lib.moe_gate_workspace_bytes(8, 256, 8) == 8 * 8 * 4
+    assert lib.moe_gate_workspace_bytes(100, 2816, 256) == 11 * 100 * 256 * 4
     for bad in ((0, 256, 8), (4, 0, 8), (4, 256, 0), (-1, 256, 8)):
         assert lib.moe_gate_workspace_bytes(*bad) == 0
 

@@ -143,7 +143,10 @@ def fused_bound(H, mag):
 @pytest.mark.parametrize("T,H,E,k", [(1, 256, 8, 2), (5, 1056, 100, 4), (16, 512, 256, 8), (17, 7168, 256, 8),
                                      (40, 2048, 64, 6), (64, 768, 33, 3), (65, 4096, 256, 8),
                                      (128, 7168, 256, 8), (130, 1024, 256, 16), (300, 7168, 32, 8),
-                                     (1024, 7168, 256, 8), (2, 64, 1, 1)])
+                                     (1024, 7168, 256, 8), (2, 64, 1, 1),
+                                     # 6 and 11 K slices: the top-k re-reads the last slice
+                                     # for the missing ones and drops them
+                                     (50, 1536, 64, 4), (100, 2816, 256, 8)])
 def test_fused_gate_matches_oracle(lib, T, H, E, k):
     ri = synth.make_router_inputs(T, H, E, seed=7 * T + H + E)
     x, wr = dev_bits(ri.x_bits), dev_bits(ri.wr_bits)
