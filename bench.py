@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer µs at 1–256 tok/GPU; dispatch/combine GB/s; grouped-GEMM TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
-GEMM1_SRC = os.path.join(ROOT, "combine_top_gate_amd", "csrc", "gemm_lowp.hip")
+# the GEMM1 kernel's source and the headers compiled into it
+GEMM1_SRC = [os.path.join(ROOT, "combine_top_gate_amd", "csrc", f)
+             for f in ("gemm_lowp.hip", "dispatch_chunk.h", "kernels.h", "pack_layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_decode128_fp8_traffic.md")
 
 
@@ -95,10 +97,12 @@ def algorithmic_bytes(inp, cnt):
     return d, flops
 
 
-def code_sha256(path):
-    """sha256 of a source file's code: // comments, trailing blanks and blank lines removed,
-    so that an edit of the comments alone keeps counters taken on the same code."""
-    lines = (re.sub(r"//.*$", "", line).rstrip() for line in open(path).read().split("\n"))
+def code_sha256(paths):
+    """sha256 of source files' code (one path or a list, hashed in order): // comments,
+    trailing blanks and blank lines removed, so that an edit of the comments alone keeps
+    counters taken on the same code."""
+    text = "".join(open(p).read() + "\n" for p in ([paths] if isinstance(paths, str) else paths))
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.split("\n"))
     return hashlib.sha256("\n".join(line for line in lines if line.strip()).encode()).hexdigest()
 
 

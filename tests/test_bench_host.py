@@ -47,3 +47,7 @@ def test_code_hash_ignores_comments_only(tmp_path):
     c.write_text("int f(int x) {  // one\n  return x + 2;\n}\n")
     assert bench.code_sha256(str(a)) == bench.code_sha256(str(b))
     assert bench.code_sha256(str(a)) != bench.code_sha256(str(c))
+    # a list of files: a change in any of them changes the hash
+    assert bench.code_sha256([str(a), str(a)]) == bench.code_sha256([str(b), str(a)])
+    assert bench.code_sha256([str(a), str(a)]) != bench.code_sha256([str(a), str(c)])
+    assert bench.code_sha256(str(a)) == bench.code_sha256([str(a)])
