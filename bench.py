@@ -168,6 +168,32 @@ def layer_distribution(torch, run, steps):
             "method": f"{steps} calls, HIP events between consecutive calls (each a queue barrier)"}
 
 
+def time_graph(torch, moe, ds, steps):
+    """Microseconds per layer call replayed from a captured HIP graph: one graph holds one
+    call per weight copy (alternating as in the timed loop), replayed back to back behind
+    a GPU spin, HIP events around all the replays."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for dd in ds:
+            moe.run(dd)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // len(ds))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(ds))
+    del g
+    return {"us_per_call": round(us, 2), "calls": reps * len(ds),
+            "method": "HIP graph of one layer call per weight copy, replayed back to back behind a GPU spin"}
+
+
 def time_combine_fp8(torch, moe, d, inp, nbytes_combine, calls=200):
     """Microseconds per FP8-output combine (the layer's output requantised 1x128 for the
     next layer) on the last layer's expert outputs, timed like the gate; its bytes are the
@@ -345,6 +371,8 @@ def main():
         raise RuntimeError("device error during the timed region")
     print("[bench] layer distribution, warm and cold dispatch / combine", file=sys.stderr, flush=True)
     dist = layer_distribution(torch, run, args.steps)
+    # the SENTINEL handshake's per-call epoch cannot be replayed from a graph
+    graph = time_graph(torch, moe, ds, args.steps) if sched == binding.MOE_SCHED_FENCE else None
     disp_warm, disp_cold = time_warm_cold(torch, lambda: moe.dispatch(inp.T_s, d.x, d.x_scale, d.ids))
     comb_warm, comb_cold = time_warm_cold(torch, lambda: moe.combine(d.topk_w, d.out))
     if args.calib_copy_mib:
@@ -389,6 +417,7 @@ def main():
                       "gemm_of_fp8_peak": round(flops / ((avg[1] + avg[2]) * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)},
         "us_per_step_with_stage_events": round((t3 - t2) * 1e6 / args.steps, 2),
         "layer_us_dist": dist,
+        "layer_us_graph": graph,
         "weight_copies": len(ds),
         "dispatch_alone": {"warm_us": round(disp_warm, 2), "cold_us": round(disp_cold, 2),
                            "warm_GBps": round(gbps(nbytes["dispatch"], disp_warm * 1e-3), 1),

@@ -515,8 +515,16 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (T_s > 0 && (!topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
   const bool timed = c->timing_n < c->timing_cap;
-  if (timed) record(c, 0, stream);
   const bool sn = sentinel_applies(c, T_s);
+  if (sn || timed) {
+    // a replayed graph would repeat this call's epoch, or its timing events
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(stream, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(MOE_ERR_INVALID_ARG, "%s cannot be captured into a graph",
+                  sn ? "a SENTINEL layer call (per-call epoch)" : "a timed layer call");
+  }
+  if (timed) record(c, 0, stream);
   moe_status st;
   DispatchArgs fused;
   const bool use_fused = sn && c->dispatch_cus == 0;

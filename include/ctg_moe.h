@@ -204,7 +204,20 @@ moe_status moe_combine(moe_ctx* ctx, const float* topk_w, void* out, hipStream_t
 moe_status moe_combine_fp8(moe_ctx* ctx, const float* topk_w, uint8_t* out, float* out_scale,
                            hipStream_t stream);
 
-/* The whole layer: dispatch, grouped GEMM and combine, synchronised per cfg.sched. */
+/*
+ * The whole layer: dispatch, grouped GEMM and combine, synchronised per cfg.sched.
+ *
+ * Graph replay (the decode step as one submitted graph [GC-MoE explainer, "Three-Node
+ * CUDA Graph and token-ring Handshake"]): under the FENCE schedule the call only
+ * enqueues kernels on `stream` (no allocation, memset, copy or host wait) and every
+ * buffer it reads is rewritten by an earlier step of the same call, so it may be
+ * captured into a HIP graph (stream capture) and the graph replayed; each replay
+ * computes the layer on what x, ids and topk_w hold at that time, with the sizes and
+ * pointers of the captured call.  moe_dispatch, moe_grouped_gemm and moe_combine may
+ * be captured likewise.  A call that takes the SENTINEL handshake (its flags carry a
+ * per-call epoch set on the host) or records timing events returns MOE_ERR_INVALID_ARG
+ * when `stream` is capturing.
+ */
 moe_status moe_layer(moe_ctx* ctx, int32_t tokens_per_src, const void* const* x,
                      const float* const* x_scale, const int32_t* ids, const float* topk_w,
                      const moe_weights* w, void* out, hipStream_t stream);
