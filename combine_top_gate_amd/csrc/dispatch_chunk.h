@@ -54,31 +54,41 @@ __device__ __forceinline__ uint64_t dispatch_lanemask_lt(int lane) {
 // warm / cold: 128 FP8 tokens 6.2 / 10.7 against 6.5 / 11.6; 256 bf16 tokens 8.3 / 13.1
 // against 9.1 / 16.5; the 4096-token prefill 51 / 73 against 60 / 73.
 template <int U>
-__device__ __forceinline__ void dispatch_copy(const DispatchArgs& a, int s, int t0, int nv, int work,
-                                              const int* s_dst) {
-  for (int w0 = threadIdx.x; w0 < work; w0 += U * kDispatchThreads) {
-    dispatch_vec4 val[U];
-    int tt[U], vv[U];
+struct DispatchCopyRegs {
+  dispatch_vec4 val[U];
+  int tt[U], vv[U];
+};
+
+// The U loads of the round that starts at vector w0 (work > 0).
+template <int U>
+__device__ __forceinline__ void dispatch_copy_load(const DispatchArgs& a, int s, int t0, int nv, int work, int w0,
+                                                   DispatchCopyRegs<U>& r) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int w = min(w0 + u * kDispatchThreads, work - 1);
+    r.tt[u] = w / nv;
+    r.vv[u] = w - r.tt[u] * nv;
+    r.val[u] = reinterpret_cast<const dispatch_vec4*>(a.src.x[s] + (int64_t)(t0 + r.tt[u]) * a.row_bytes)[r.vv[u]];
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void dispatch_copy_store(const DispatchArgs& a, int work, int w0,
+                                                    const DispatchCopyRegs<U>& r, const int* s_dst) {
+  for (int j = 0; j < a.k; ++j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int w = min(w0 + u * kDispatchThreads, work - 1);
-      tt[u] = w / nv;
-      vv[u] = w - tt[u] * nv;
-      val[u] = reinterpret_cast<const dispatch_vec4*>(a.src.x[s] + (int64_t)(t0 + tt[u]) * a.row_bytes)[vv[u]];
-    }
-    for (int j = 0; j < a.k; ++j) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = s_dst[tt[u] * a.k + j];
-        if (w0 + u * kDispatchThreads < work && r >= 0)
-          reinterpret_cast<dispatch_vec4*>(a.win + (int64_t)r * a.row_bytes)[vv[u]] = val[u];
-      }
+      const int row = s_dst[r.tt[u] * a.k + j];
+      if (w0 + u * kDispatchThreads < work && row >= 0)
+        reinterpret_cast<dispatch_vec4*>(a.win + (int64_t)row * a.row_bytes)[r.vv[u]] = r.val[u];
     }
   }
 }
 
-// Workgroup-uniform: chunk p (tokens [p*tpb, (p+1)*tpb)) of source s, of `chunks`.
-__device__ __forceinline__ void dispatch_chunk(const DispatchArgs& a, int s, int p, int chunks, DispatchSmem& sm) {
+// Workgroup-uniform: chunk p (tokens [p*tpb, (p+1)*tpb)) of source s, of `chunks`, with
+// U loads per thread per copy round.
+template <int U>
+__device__ __forceinline__ void dispatch_chunk_u(const DispatchArgs& a, int s, int p, int chunks, DispatchSmem& sm) {
   int* s_hist = sm.hist;
   int* s_run = sm.run;
   int (*s_wcnt)[MOE_MAX_EXPERTS] = sm.wcnt;
@@ -90,6 +100,12 @@ __device__ __forceinline__ void dispatch_chunk(const DispatchArgs& a, int s, int
   const int i0 = t0 * a.k, i1 = t1 * a.k;
   const int base = s * n;
   const int32_t* ids = a.ids + base;
+  // the copy's first round of loads goes out now: the source rows' addresses do not depend
+  // on the routing below, so their latency overlaps it
+  const int nv = a.row_bytes >> 4;
+  const int work = (t1 - t0) * nv;
+  DispatchCopyRegs<U> first;
+  if (work > 0) dispatch_copy_load<U>(a, s, t0, nv, work, tid, first);
 
   for (int e = tid; e < MOE_MAX_EXPERTS; e += kDispatchThreads) {
     s_hist[e] = 0;
@@ -184,12 +200,12 @@ __device__ __forceinline__ void dispatch_chunk(const DispatchArgs& a, int s, int
   }
 
   // copy: each token row is read once as 16-byte vectors and written to its k rows
-  const int nv = a.row_bytes >> 4;
-  const int work = (t1 - t0) * nv;
-  if (work > 2 * kDispatchThreads)
-    dispatch_copy<4>(a, s, t0, nv, work, s_dst);
-  else
-    dispatch_copy<2>(a, s, t0, nv, work, s_dst);
+  if (tid < work) dispatch_copy_store<U>(a, work, tid, first, s_dst);
+  for (int w0 = tid + U * kDispatchThreads; w0 < work; w0 += U * kDispatchThreads) {
+    DispatchCopyRegs<U> r;
+    dispatch_copy_load<U>(a, s, t0, nv, work, w0, r);
+    dispatch_copy_store<U>(a, work, w0, r, s_dst);
+  }
   if (a.nsc) {
     const int swork = (t1 - t0) * a.nsc;
     for (int w = tid; w < swork; w += kDispatchThreads) {
@@ -212,4 +228,12 @@ __device__ __forceinline__ void dispatch_chunk(const DispatchArgs& a, int s, int
       }
     }
   }
+}
+
+__device__ __forceinline__ void dispatch_chunk(const DispatchArgs& a, int s, int p, int chunks, DispatchSmem& sm) {
+  const int t0 = p * a.tpb, t1 = min(a.T_s, t0 + a.tpb);
+  if ((t1 - t0) * (a.row_bytes >> 4) > 2 * kDispatchThreads)
+    dispatch_chunk_u<4>(a, s, p, chunks, sm);
+  else
+    dispatch_chunk_u<2>(a, s, p, chunks, sm);
 }
