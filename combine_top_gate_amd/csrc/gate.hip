@@ -280,7 +280,8 @@ int gate_split(int T, int H, int E) {
   // at least 8 K steps (two per wave) in every slice.  Measured on MI355X (H 7168, 256
   // experts, gate call in us), against every fixed split of 1-16: the rule's choice is the
   // fastest or within 0.1 us of it from 1 to 4096 tokens (e.g. 8.6 at 8 tokens, 11.1 at
-  // 64, 13.6 at 128, 39.3 at 1024).
+  // 64, 13.6 at 128, 39.3 at 1024); aiming at 384-1024 workgroups instead (up to 28
+  // slices) was slower at every size (15.8 us at 128 tokens, 9.6 at 8).
   const int tiles = ((E + 15) / 16) * ((T + 127) / 128);
   const int ks = (256 + tiles - 1) / tiles;
   return std::max(1, std::min({ks, kGateMaxSplit, H / 256}));
