@@ -214,7 +214,7 @@ def h_format(act):
     return {"fp8": "fp8", "bf16": "bf16"}.get(act)
 
 
-def expert_ffn(x, w13, w2, inter, requant):
+def expert_ffn(x, w13, w2, inter, requant, pre=None):
     """Dequantised rows x [M][H], W13 [2I][H], W2 [H][I] -> (y [M][H], h_codes, h_scales).
 
     y = requant(silu(x W13[:I]^T) * (x W13[I:]^T)) W2^T, all in fp64.  requant: "fp8"
@@ -225,8 +225,12 @@ def expert_ffn(x, w13, w2, inter, requant):
     [GC-MoE explainer, "Two MMA Implementations in the Compute Partition"]; the pages do
     not fix the activations' precision there, and the reading taken is that x and h stay
     bf16 (h rounded from its exact value).
+    pre: when a dict is given, the exact gate|up projections a [M][2I] are left in
+    pre["a"] (for tests that bound the rounding of h; nothing else changes).
     """
     a = x @ w13.T
+    if pre is not None:
+        pre["a"] = a
     h = swiglu(a, inter)
     if requant == "bf16":
         hq, hs = codecs.bf16_round(h), None
@@ -301,7 +305,7 @@ def _act_rows(inp):
     return np.asarray(x, dtype=np.float64).reshape(S * T_s, H)
 
 
-def moe_layer(inp):
+def moe_layer(inp, experts=None, on_expert=None):
     """Run the whole layer on the CPU; returns every intermediate the GPU exposes.
 
     inp has fields: S, T_s, H, I, E, k, act ("f32"|"fp8"|"bf16", the last as bf16
@@ -310,6 +314,18 @@ def moe_layer(inp):
     x_scale [S][T_s][H/128] or None, ids [S][T_s][k], topk_w [S][T_s][k],
     w13, s13, w2, s2 (per expert, leading dim E) and sh_w13, sh_s13, sh_w2,
     sh_s2 for the shared expert.
+
+    Two conveniences for tests that check a GPU's intermediate results expert by expert
+    (neither changes what is computed):
+      experts    None (all), or the routed expert ids to evaluate, plus "shared" for the
+                 shared expert; the window rows of the others stay zero, and so does
+                 their share of "out".
+      on_expert  called after each evaluated expert as on_expert(e, rows, x_rows, w13,
+                 w2, a, y, hq, hs): e is the expert id or "shared", rows its window rows
+                 (None for the shared expert, whose rows are all tokens in order),
+                 x_rows/w13/w2 the dequantised operands, a the exact gate|up
+                 projections, y the output rows rounded to the output format, hq/hs what
+                 h became (codes and scales, bf16 values, or None).
     """
     S, T_s, H, I, E, k = inp.S, inp.T_s, inp.H, inp.I, inp.E, inp.k
     hfmt = h_format(inp.act)
@@ -325,24 +341,30 @@ def moe_layer(inp):
     h_bf16 = np.zeros((R, I), dtype=np.float64) if hfmt == "bf16" else None
     for e in range(E):
         r = rows[e]
-        if len(r) == 0:
+        if len(r) == 0 or (experts is not None and e not in experts):
             continue
         w13 = dequant_weight(inp.weight, inp.w13[e], None if inp.s13 is None else inp.s13[e])
         w2 = dequant_weight(inp.weight, inp.w2[e], None if inp.s2 is None else inp.s2[e])
-        y, hq, hs = expert_ffn(xt[src_token[r]], w13, w2, I, hfmt)
+        pre = {} if on_expert else None
+        y, hq, hs = expert_ffn(xt[src_token[r]], w13, w2, I, hfmt, pre)
         y_win[r] = round_out(y, inp.out)
         if requant:
             h_codes[r] = hq
             h_scales[r] = hs
         elif hfmt == "bf16":
             h_bf16[r] = hq
+        if on_expert:
+            on_expert(e, r, xt[src_token[r]], w13, w2, pre["a"], y_win[r], hq, hs)
     y_sh = None
     sh = {}
-    if inp.shared_I:
+    if inp.shared_I and (experts is None or "shared" in experts):
         w13 = dequant_weight(inp.weight, inp.sh_w13, inp.sh_s13)
         w2 = dequant_weight(inp.weight, inp.sh_w2, inp.sh_s2)
-        y_sh, shq, shs = expert_ffn(xt, w13, w2, inp.shared_I, hfmt)
+        pre = {} if on_expert else None
+        y_sh, shq, shs = expert_ffn(xt, w13, w2, inp.shared_I, hfmt, pre)
         y_sh = round_out(y_sh, inp.out)
+        if on_expert:
+            on_expert("shared", None, xt, w13, w2, pre["a"], y_sh, shq, shs)
         sh = {"y_shared": y_sh, "h_shared_codes": shq if requant else None, "h_shared_scales": shs,
               "h_shared_bf16": shq if hfmt == "bf16" else None}
     out = combine(y_win, route["dst_row"], inp.topk_w, y_sh)

@@ -1,0 +1,390 @@
+"""Parity checks of the HIP path against the CPU oracle (helpers of the GPU tests and of
+the smoke check; test infrastructure, not collected by pytest).
+
+Integers (counts, offsets, window rows, row sources) and dispatched bytes are compared
+bit for bit.  Floating outputs use the statistic
+    err_i = |g_i - r_i| / max(|r_i|, rms(r))
+(the reference's magnitude, floored at the rms of the array compared, so that elements
+near zero are judged against the array's scale), and per row ||g_t - r_t||_2 / ||r_t||_2.
+Bounds: 1e-3 for the fp32 layer, 2e-2 for the FP8 and W4A16 layers, elementwise and per
+row.
+
+FP8 layers.  The 1x128 FP8 requantisation of the SwiGLU output is a step function.  The
+pages fix no accumulation order or precision inside the FP8 block GEMM, so where the
+exact SwiGLU value lies within the GEMM's accumulation error of an e4m3 rounding
+midpoint, both neighbouring codes are results of the method, and one code step reaches
+every output of its row (test_tolerance_premise.py shows the oracle's own output moving by
+more than 2e-2 elementwise under a 1e-5 relative change of h).  So:
+  1. every GPU h code must be a correct rounding of some value inside a band around the
+     oracle's exact h, derived from the oracle's own fp64 values: the MFMA truncates
+     each group of 8 products by less than 7 * 2^(Emax - 13) (Emax the group's largest
+     exponent sum; pinned on the GPU in test_gpu_probe.py) and adds the group sums in
+     fp32, so a GEMM1 output is off by at most Tr + gamma_n (sum|terms| + Tr) with
+     Tr = 7 * 2^-13 * sum_g (largest code binades of the group's x and w, block scales
+     included) and n = 16 + 2 H/128 + 8; the band of h follows through SwiGLU (first and
+     second order).  Since that bound takes every truncation at its worst, codes outside
+     the much narrower plain-fp32 band (gamma_n, n = 128 + 2 H/128 + 8) must stay rare
+     (at most 1e-4 of them, plus one).  Scales within the band of their block's amax.
+  2. the effect of the codes that differ from the oracle's is computed from the oracle's
+     values (|dh| times W2): per y row an L2 allowance sum_c |dh_c| ||W2[:, c]||, per
+     element sum_c |dh_c| |W2[n][c]|; an output row carries the allowances of the rows it
+     sums times their |gate weight|, plus the shared expert's.
+  3. what the allowance does not explain must be within the bound, per row and
+     elementwise:  ||g_t - r_t|| - allow_t <= tol ||r_t||  and
+     max(|g_i - r_i| - allow_i, 0) / max(|r_i|, rms(r)) <= tol.
+W4A16 layers (bf16 activations and h, no requantisation): every h element within the
+bf16 rounding of an fp32-accumulation band around the exact value, y rows and outputs
+within the bound with no allowance, and each output row within one bf16 rounding.
+
+The oracle runs expert by expert (layer.moe_layer's on_expert hook), so each expert's
+checks use the operands the oracle already holds and the full-size configurations are
+checked on every row and every token.
+"""
+import numpy as np
+import torch
+
+from combine_top_gate_amd import binding
+from oracle import codecs, layer
+
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+U32 = 2.0 ** -24
+
+
+# ------------------------------------------------------------------ statistics
+def rel_err(g, r):
+    """max_i |g_i - r_i| / max(|r_i|, rms(r))."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.size == 0:
+        return 0.0
+    scale = np.sqrt(np.mean(r ** 2))
+    if scale == 0:
+        return float(np.max(np.abs(g)))
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), scale)))
+
+
+class Stats:
+    """Largest statistics seen by close_rows, by label (printed by the tests)."""
+
+    def __init__(self):
+        self.worst = {}
+
+    def add(self, label, row, el):
+        r0, e0 = self.worst.get(label, (0.0, 0.0))
+        self.worst[label] = (max(r0, row), max(e0, el))
+
+    def report(self):
+        for label, (row, el) in sorted(self.worst.items()):
+            print(f"  {label}: row relL2 after allowance max {row:.3e} | elementwise after allowance max "
+                  f"{el:.3e}", flush=True)
+
+
+def close_rows(gy, ry, tol, allow=None, allow_el=None, stats=None, label="rows"):
+    """Per row ||g - r|| - allow <= tol ||r||, and elementwise max(|g - r| - allow_el, 0) /
+    max(|r|, rms(r)) <= tol (rms over the rows given).  allow/allow_el None: zero."""
+    gy = np.asarray(gy, np.float64)
+    ry = np.asarray(ry, np.float64)
+    if ry.size == 0:
+        return True
+    gy = gy.reshape(-1, gy.shape[-1])
+    ry = ry.reshape(-1, ry.shape[-1])
+    num = np.linalg.norm(gy - ry, axis=1)
+    den = np.linalg.norm(ry, axis=1)
+    excess = num if allow is None else np.maximum(num - allow, 0.0)
+    row = np.where(den > 0, excess / np.where(den > 0, den, 1.0), excess)
+    scale = np.sqrt(np.mean(ry ** 2))
+    diff = np.abs(gy - ry)
+    if allow_el is not None:
+        diff = np.maximum(diff - allow_el, 0.0)
+    e = diff / np.maximum(np.abs(ry), scale if scale > 0 else 1.0)
+    rmax, emax = float(row.max()), float(e.max())
+    if stats is not None:
+        stats.add(label, rmax, emax)
+    ok = rmax <= tol and emax <= tol
+    if not ok:
+        i = np.unravel_index(int(np.argmax(e)), e.shape)
+        print(f"  {label}: row relL2 max {rmax:.3e}, elementwise max {emax:.3e} at {i}: gpu {gy[i]:.6e} "
+              f"oracle {ry[i]:.6e} allowance {0.0 if allow_el is None else allow_el[i]:.3e}", flush=True)
+    return ok
+
+
+# ------------------------------------------------------------- error bands
+def group_binades_act(codes, scales):
+    """Per 8-k group, the largest code binade 2^max(e, emin) times the block scale: FP8
+    activations [M][K] with 1x128 scales [M][K/128] -> [M][K/8] (a zero code counts
+    with emin, which only widens the bound)."""
+    c = np.asarray(codes, np.uint8)
+    ex = np.maximum((c >> 3) & 15, 1)
+    gm = ex.reshape(c.shape[0], -1, 8).max(-1).astype(np.int64) - 7
+    return np.ldexp(1.0, gm) * np.repeat(np.asarray(scales, np.float64), 16, axis=1)
+
+
+def group_binades_w(fmt, w, s):
+    """The same for a weight matrix [N][K]: FP8 codes with 128x128 scales, or packed
+    e2m1 codes [N][K/2] (even k in the low nibble) with e8m0 scales per 32 k."""
+    w = np.asarray(w, np.uint8)
+    N = w.shape[0]
+    if fmt == "fp8":
+        ex = np.maximum((w >> 3) & 15, 1)
+        gm = ex.reshape(N, -1, 8).max(-1).astype(np.int64) - 7
+        sc = np.repeat(np.repeat(np.asarray(s, np.float64), 128, axis=0), 16, axis=1)
+    else:
+        # exponent fields of the low and high nibble of each byte; 8 k = 4 bytes
+        ex = np.maximum(np.maximum((w >> 1) & 3, (w >> 5) & 3), 1)
+        gm = ex.reshape(N, -1, 4).max(-1).astype(np.int64) - 1
+        sc = np.repeat(codecs.e8m0_decode(s), 4, axis=1)
+    return np.ldexp(1.0, gm) * sc
+
+
+def fp8_requant_check(x_rows, xg, w13, wg, w2, inter, a, ref_codes, ref_scales, g_codes, g_scales):
+    """Checks requantised SwiGLU codes against the GEMM's error band (module docstring,
+    step 1); returns the y-row allowance (fp64 [M], an L2 bound) and the per-element
+    allowance (fp64 [M][H]) that the code differences explain (step 2).
+
+    x_rows: dequantised activations [M][H]; w13/w2: dequantised weights; a: the exact
+    gate|up projections x_rows w13^T (the oracle's); xg/wg: per 8-k group binade maxima
+    of x_rows and w13 (group_binades_*); ref_*: the oracle's codes and scales; g_*: the
+    GPU's.
+    """
+    H = x_rows.shape[1]
+    mag = np.abs(x_rows) @ np.abs(w13).T
+    g, u = a[:, :inter], a[:, inter:2 * inter]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sg
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    h = silu * u
+    M = h.shape[0]
+    s = np.repeat(ref_scales, 128, axis=1)
+
+    def h_band(ea, gam):
+        eg, eu = ea[:, :inter], ea[:, inter:]
+        # |d silu / dg| <= 1.1, |d2 silu / dg2| <= 0.5
+        return (np.abs(dsilu * u) * eg + np.abs(silu) * eu + 1.1 * eg * eu + 0.25 * np.abs(u) * eg ** 2
+                + gam * np.abs(h))
+
+    def code_range(band):
+        """The e4m3 values a value inside the band can round to, and the scale's band."""
+        # the GPU's scale may differ by the band of its block's largest element
+        ds = np.zeros_like(ref_scales)
+        for b in range(inter // 128):
+            am = np.argmax(np.abs(h[:, b * 128:(b + 1) * 128]), axis=1) + b * 128
+            amax = np.abs(h[np.arange(M), am])
+            ds[:, b] = np.where(amax > 0, band[np.arange(M), am] / np.where(amax > 0, amax, 1.0), 0.0)
+        v = h / s
+        dv = band / s + np.abs(v) * (np.repeat(ds, 128, axis=1) + 4 * U32)
+        lo = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(v - dv, -448.0, 448.0)))
+        hi = codecs.e4m3_decode(codecs.e4m3_encode(np.clip(v + dv, -448.0, 448.0)))
+        return lo, hi, ds, v, dv
+
+    n = 16 + 2 * (H // 128) + 8
+    gam = n * U32 / (1 - n * U32)
+    tr = 7 * 2.0 ** -13 * (xg @ wg.T)
+    band = h_band(tr + gam * (mag + tr), gam)
+    lo, hi, ds, v, dv = code_range(band)
+    n32 = 128 + 2 * (H // 128) + 8
+    gam32 = n32 * U32 / (1 - n32 * U32)
+    lo32, hi32, _, _, _ = code_range(h_band(gam32 * mag, gam32))
+    gv = codecs.e4m3_decode(g_codes)
+    rv = codecs.e4m3_decode(ref_codes)
+    bad = (gv < lo) | (gv > hi)
+    out32 = (gv < lo32) | (gv > hi32)
+    if bad.any() or out32.any():
+        i, c = (int(q[0]) for q in np.nonzero(bad if bad.any() else out32))
+        b = c // 128
+        print(f"  {int(bad.sum())} codes outside the bound, {int(out32.sum())} outside the fp32 band (of "
+              f"{bad.size}), e.g. row {i} col {c}: h {h[i, c]:.9e} band {band[i, c]:.3e} v {v[i, c]:.9e} dv "
+              f"{dv[i, c]:.3e} lo {lo[i, c]} hi {hi[i, c]} (fp32 {lo32[i, c]} {hi32[i, c]}) gpu {gv[i, c]} "
+              f"oracle {rv[i, c]} | scale gpu {g_scales[i, b]:.9e} oracle {ref_scales[i, b]:.9e}", flush=True)
+    assert not bad.any(), "an h code outside the accumulation bound"
+    assert out32.sum() <= 1e-4 * out32.size + 1, f"{int(out32.sum())} h codes outside the fp32 band"
+    assert np.all(np.abs(g_scales - ref_scales) <= ref_scales * (ds + 4 * U32)), "h scale outside band"
+    dh = np.abs(gv - rv) * s                                 # |h_gpu - h_oracle| after dequantisation
+    col = np.linalg.norm(w2, axis=0)                         # ||w2[:, c]||
+    # sum_c |dh_c| |w2[n][c]|, over the (few) rows and columns holding a differing code
+    allow_el = np.zeros((M, w2.shape[0]))
+    rnz, cnz = np.nonzero(dh.any(axis=1))[0], np.nonzero(dh.any(axis=0))[0]
+    if len(rnz):
+        allow_el[rnz] = dh[np.ix_(rnz, cnz)] @ np.abs(w2[:, cnz]).T
+    return dh @ col, allow_el, int((gv != rv).sum()), int(out32.sum())
+
+
+def bf16_h_check(x_rows, w13, inter, a, g_h):
+    """W4A16: the GPU's bf16 h against the oracle's exact SwiGLU value, elementwise:
+    |g - h| <= band + 2^-8 (|h| + band).  band bounds the GPU's value before rounding:
+    Higham's gamma_n (n = H + 16) times the sum of |terms| of the gate and up dot products,
+    carried through SwiGLU, plus gamma_n |h|.  Rounding that value to bf16 (8 significant
+    bits, to nearest) moves it by at most 2^-8 of its magnitude.
+    Returns the largest |g - h| / bound."""
+    H = x_rows.shape[1]
+    n = H + 16
+    gam = n * U32 / (1 - n * U32)
+    mag = np.abs(x_rows) @ np.abs(w13).T
+    g, u = a[:, :inter], a[:, inter:2 * inter]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sg
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    h = silu * u
+    band = gam * (np.abs(dsilu * u) * mag[:, :inter] + np.abs(silu) * mag[:, inter:] + np.abs(h))
+    bound = band + 2.0 ** -8 * (np.abs(h) + band) + 1e-30
+    r = np.abs(g_h - h) / bound
+    assert np.all(r <= 1.0), f"h outside its bound by {r.max():.3f}"
+    return float(r.max())
+
+
+# -------------------------------------------------------------- GPU state
+def bf16_np(t):
+    """bf16 tensor (or its int16 view) -> fp64 numpy."""
+    u = t.contiguous().view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore", over="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def out_np(inp, t):
+    return bf16_np(t) if inp.out == "bf16" else t.cpu().numpy().astype(np.float64)
+
+
+def run(inp, moe=None, max_tokens=None, packed=False, opts=None):
+    print(f"[gpu case] {inp.name} S={inp.S} T_s={inp.T_s} H={inp.H} I={inp.I} E={inp.E} "
+          f"k={inp.k} w={inp.weight} shared={inp.shared_I} packed={packed} opts={opts}", flush=True)
+    moe = moe or binding.Moe.for_inputs(inp, max_tokens=max_tokens)
+    for o, v in (opts or {}).items():
+        moe.set_option(o, v)
+    d = binding.DeviceInputs(inp)
+    if packed:
+        moe.pack(d)
+    moe.run(d)
+    torch.cuda.synchronize()
+    return moe, d
+
+
+def gpu_state(moe, inp, rows_only=False):
+    """The context's routing and, unless rows_only, its windows, h (+ scales) and y, as
+    numpy arrays (rows 0..R-1 routed, R..R+T-1 the shared expert)."""
+    S, T_s, k, E, H = inp.S, inp.T_s, inp.k, inp.E, inp.H
+    R, T = S * T_s * k, S * T_s
+    cnt, off, dst, src = (t.cpu().numpy() for t in moe.routing(S, T_s, k, E))
+    torch.cuda.synchronize()
+    st = {"cnt": cnt, "off": off, "dst_row": dst, "row_src": src}
+    if rows_only:
+        return st
+    hstride = max(inp.I, inp.shared_I)
+    if inp.act == "fp8":
+        st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H).cpu().numpy().reshape(R, H)
+        st["wsc"] = moe.buffer(binding.MOE_BUF_WSCALE, R * (H // 128) * 4).cpu().numpy().view(
+            np.float32).reshape(R, H // 128)
+        st["h"] = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride).cpu().numpy().reshape(R + T, hstride)
+        st["hs"] = moe.buffer(binding.MOE_BUF_HSCALE, (R + T) * (hstride // 128) * 4).cpu().numpy().view(
+            np.float32).reshape(R + T, hstride // 128)
+        y = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 2)
+        st["y"] = bf16_np(y.view(torch.int16)).reshape(R + T, H)
+    elif inp.act == "bf16":
+        st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H * 2).cpu().numpy().view(np.uint16).reshape(R, H)
+        h = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride * 2)
+        st["h"] = bf16_np(h.view(torch.int16)).reshape(R + T, hstride)
+        y = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 2)
+        st["y"] = bf16_np(y.view(torch.int16)).reshape(R + T, H)
+    else:
+        st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H * 4).cpu().numpy().view(np.float32).reshape(R, H)
+        st["h"] = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride * 4).cpu().numpy().view(
+            np.float32).reshape(R + T, hstride).astype(np.float64)
+        st["y"] = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 4).cpu().numpy().view(
+            np.float32).reshape(R + T, H).astype(np.float64)
+    torch.cuda.synchronize()
+    return st
+
+
+def check_routing(g, ref):
+    assert np.array_equal(g["cnt"], ref["cnt"])
+    assert np.array_equal(g["off"], ref["off"])
+    assert np.array_equal(g["dst_row"], ref["dst_row"])
+    assert np.array_equal(g["row_src"], ref["row_src"])
+
+
+# ------------------------------------------------------------ whole layer
+def check_layer(inp, g, out, stats=None, check_windows=True):
+    """The whole layer against the oracle: routing bit-exact, dispatched rows (and scales)
+    bit-exact, h per its format's rule, y rows, shared rows and the combined output within
+    the bound (module docstring).  g: gpu_state(); out: the layer output as fp64 numpy.
+    Returns the oracle's result."""
+    stats = stats if stats is not None else Stats()
+    S, T_s, k, H = inp.S, inp.T_s, inp.k, inp.H
+    T, R = S * T_s, S * T_s * k
+    tol = TOL[inp.out]
+    route = layer.dispatch(inp.ids, inp.E)
+    check_routing(g, route)
+    row_src = route["row_src"]
+    used = row_src >= 0
+    if check_windows:
+        xs = np.asarray(inp.x).reshape(T, -1)
+        assert np.array_equal(g["win"][used], xs[row_src[used] // k]), "window bytes differ"
+        if inp.act == "fp8":
+            assert np.array_equal(g["wsc"][used], np.asarray(inp.x_scale).reshape(T, -1)[row_src[used] // k])
+    wabs = np.abs(np.asarray(inp.topk_w, np.float64).reshape(-1))
+    allow_out = np.zeros(T)
+    allow_out_el = np.zeros((T, H))
+    counts = {"codes": 0, "flipped": 0, "outside_fp32_band": 0, "h_bound_max": 0.0}
+    if inp.act == "fp8":
+        xc = np.asarray(inp.x).reshape(T, H)
+        xg_all = group_binades_act(xc, np.asarray(inp.x_scale).reshape(T, H // 128))
+
+    def hook(e, rows, x_rows, w13, w2, a, y, hq, hs):
+        shared = rows is None
+        inter = inp.shared_I if shared else inp.I
+        grows = np.arange(R, R + T) if shared else rows
+        label = "shared y rows" if shared else "window y rows"
+        if inp.act == "f32":
+            h = layer.swiglu(a, inter)
+            assert rel_err(g["h"][grows, :inter], h) <= 1e-4, f"h of expert {e}"
+            assert rel_err(g["y"][grows], y) <= tol, f"y of expert {e}"
+            return
+        if inp.act == "bf16":
+            counts["h_bound_max"] = max(counts["h_bound_max"],
+                                        bf16_h_check(x_rows, w13, inter, a, g["h"][grows, :inter]))
+            assert close_rows(g["y"][grows], y, tol, stats=stats, label=label), f"y of expert {e}"
+            return
+        if shared:
+            wg = group_binades_w(inp.weight, inp.sh_w13, inp.sh_s13)
+            xg = xg_all
+        else:
+            wg = group_binades_w(inp.weight, inp.w13[e], None if inp.s13 is None else inp.s13[e])
+            xg = xg_all[row_src[rows] // k]
+        allow, allow_el, nflip, n32 = fp8_requant_check(
+            x_rows, xg, w13, wg, w2, inter, a, hq, hs, g["h"][grows, :inter],
+            g["hs"][grows, :inter // 128].astype(np.float64))
+        counts["codes"] += hq.size
+        counts["flipped"] += nflip
+        counts["outside_fp32_band"] += n32
+        assert close_rows(g["y"][grows], y, tol, allow, allow_el, stats, label), f"y of expert {e}"
+        if shared:
+            allow_out[:] += allow
+            allow_out_el[:] += allow_el
+        else:
+            p = row_src[rows]
+            t = p // k
+            wv = wabs[p]
+            np.add.at(allow_out, t, wv * allow)
+            if len(np.unique(t)) == len(t):
+                allow_out_el[t] += wv[:, None] * allow_el
+            else:
+                np.add.at(allow_out_el, t, wv[:, None] * allow_el)
+
+    ref = layer.moe_layer(inp, on_expert=hook)
+    rout = np.asarray(ref["out"]).reshape(T, H)
+    gout = np.asarray(out, np.float64).reshape(T, H)
+    assert np.isfinite(gout).all()
+    if inp.act == "f32":
+        assert rel_err(gout, rout) <= tol
+    elif inp.act == "bf16":
+        print(f"  h: largest |g - h| / bound {counts['h_bound_max']:.3f}", flush=True)
+        assert close_rows(gout, rout, tol, stats=stats, label="output")
+        # every activation is bf16: the error is a few bf16 roundings, not an e4m3 step;
+        # each output row within one bf16 rounding (2^-8) of the oracle's
+        num = np.linalg.norm(gout - rout, axis=1)
+        den = np.maximum(np.linalg.norm(rout, axis=1), 1e-30)
+        assert np.all(num <= 2.0 ** -8 * den), float(np.max(num / den))
+    else:
+        print(f"  h codes: {counts['flipped']} of {counts['codes']} differ from the oracle's, "
+              f"{counts['outside_fp32_band']} outside the plain-fp32 band", flush=True)
+        assert close_rows(gout, rout, tol, allow_out, allow_out_el, stats, "output")
+    stats.report()
+    return ref

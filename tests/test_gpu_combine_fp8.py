@@ -42,10 +42,16 @@ def run_fp8_out(inp, packed):
     torch.cuda.synchronize()
     R, T, H = inp.S * inp.T_s * inp.k, inp.S * inp.T_s, inp.H
     ybytes = (R + T) * H * (4 if inp.out == "f32" else 2)
-    yb = moe.buffer(binding.MOE_BUF_Y, ybytes)
-    y = yb.cpu().numpy().view(np.float32).astype(np.float64) if inp.out == "f32" else bf16_np(yb.view(torch.int16))
-    y = y.reshape(R + T, H)
     dst = moe.routing(inp.S, inp.T_s, inp.k, inp.E)[2].cpu().numpy()
+    # only the rows the combine reads were written by this call: the routed rows dst_row
+    # names and, with a shared expert, rows R..R+T-1; the others are left as zeros
+    written = np.zeros(R + T, dtype=bool)
+    written[dst[dst >= 0]] = True
+    written[R:] = inp.shared_I > 0
+    yb = moe.buffer(binding.MOE_BUF_Y, ybytes).cpu().numpy().reshape(R + T, -1)
+    yb[~written] = 0
+    y = yb.view(np.float32).astype(np.float64) if inp.out == "f32" else bf16_np(torch.from_numpy(yb.view(np.int16)))
+    y = y.reshape(R + T, H)
     assert moe.device_error() == 0
     return moe, d, q.cpu().numpy(), sc.cpu().numpy().astype(np.float64), y, dst
 

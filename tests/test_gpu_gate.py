@@ -184,12 +184,13 @@ def test_fused_gate_short_workspace_rejected(lib):
 
 def test_gate_drives_the_layer(lib):
     """The gate ahead of dispatch: the GPU gate's ids and weights go device to device into
-    the layer.  The oracle runs its own gate (fp64 router logits, top-k softmax) on the
-    same bf16 router inputs and its layer on its own ids and weights; wherever the two
-    gates chose the same ids, the layer outputs agree to the FP8 criterion (the gates'
-    weights differ only by fp32 rounding)."""
-    from oracle import layer
-    from test_gpu_parity import close, out_np
+    the layer.  The gate's choices are checked against the oracle's own gate (fp64 router
+    logits, top-k softmax) on the same bf16 router inputs: the same ids for nearly every
+    token (the two differ only where fp32 and fp64 sums order two logits differently), and
+    nearly the same weights where the ids agree (their exact bound is the fused-gate test's).  The layer is checked against
+    the oracle's layer run on the ids and weights the GPU gate produced."""
+    from oracle import layer  # noqa: F401  (the layer oracle runs inside parity.check_layer)
+    from parity import check_layer, gpu_state, out_np
     inp = synth.make_inputs("decode128_fp8", S=4, T_s=16, H=1024, I=256, E=32, k=8, seed=71)
     S, T_s, k = inp.S, inp.T_s, inp.k
     T = S * T_s
@@ -201,14 +202,16 @@ def test_gate_drives_the_layer(lib):
     d.topk_w = w.view(S, T_s, k)
     moe.run(d)
     torch.cuda.synchronize()
-    # the oracle's gate and layer, from the generator's inputs only
+    # the oracle's gate, from the generator's router inputs only
     r = gating.router_logits(codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits))
     rid, rw = gating.softmax_topk(r, k)
-    inp.ids = rid.reshape(S, T_s, k).astype(np.int32)
-    inp.topk_w = rw.astype(np.float32).reshape(S, T_s, k)
-    ref = layer.moe_layer(inp)
-    same = np.all(ids.cpu().numpy() == rid, axis=1)
+    g_ids, g_w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    same = np.all(g_ids == rid, axis=1)
     print(f"  {int(same.sum())} of {T} tokens routed alike", flush=True)
     assert same.mean() > 0.9
-    g = out_np(inp, d.out).reshape(T, inp.H)
-    assert close(g[same], np.asarray(ref["out"]).reshape(T, inp.H)[same], 2e-2)
+    assert np.allclose(g_w[same], rw[same], rtol=1e-3, atol=0)
+    # the layer on the GPU gate's own routing
+    inp.ids = g_ids.reshape(S, T_s, k).astype(np.int32)
+    inp.topk_w = g_w.astype(np.float32).reshape(S, T_s, k)
+    check_layer(inp, gpu_state(moe, inp), out_np(inp, d.out))
+    assert moe.device_error() == 0
