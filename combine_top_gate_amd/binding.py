@@ -93,6 +93,7 @@ def load():
         "moe_mfma_fp8_probe": (ctypes.c_int64, [VP, I32, I32, VP]),
         "moe_mfma_dot16x16": (st, [I32, VP, VP, VP, VP]),
         "moe_gate": (st, [I32, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP, VP, VP, VP]),
+        "moe_gate_noalloc": (st, [I32, I32, I32, I32, VP, VP, VP, VP, VP, VP]),
         "moe_status_str": (ctypes.c_char_p, [st]),
         "moe_last_error_message": (ctypes.c_char_p, []),
     }
@@ -151,6 +152,21 @@ def gate(x, wr, k, workspace=None, want_logits=False):
     _check(lib.moe_gate(T, H, E, k, _ptr(x), _ptr(wr), _ptr(workspace), nbytes, _ptr(logits), _ptr(ids),
                         _ptr(w), _stream()))
     return (ids, w, logits) if want_logits else (ids, w)
+
+
+def gate_noalloc(x, wr, k, ids=None, w=None, logits=None):
+    """The fused gate with its partial sums in the library's fixed scratch (no workspace,
+    no allocation inside the call); ids [T][k] int32, w [T][k] fp32 and logits [T][E] fp32
+    (optional) are caller tensors, allocated here when not given.  Returns (ids, w, logits)."""
+    lib = load()
+    T, H = x.shape
+    E = wr.shape[0]
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(lib.moe_gate_noalloc(T, H, E, k, _ptr(x), _ptr(wr), _ptr(logits), _ptr(ids), _ptr(w), _stream()))
+    return ids, w, logits
 
 
 def mfma_fp8_probe(sink, blocks, iters):

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -746,8 +747,13 @@ size_t moe_gate_workspace_bytes(int32_t T, int32_t H, int32_t E) {
   return (size_t)gate_split(T, H, E) * (size_t)T * (size_t)E * sizeof(float);
 }
 
-moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, void* workspace,
-                    size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream) {
+}  // extern "C"
+
+// Argument checks of the fused gate (nothing is enqueued); workspace may be null when
+// need_ws is false.
+static moe_status gate_check(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr,
+                             const void* workspace, bool need_ws, const float* logits, const int32_t* ids,
+                             const float* w) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T %d < 0", T);
   if (H <= 0 || H % 32) return fail(MOE_ERR_INVALID_ARG, "H %d is not a positive multiple of 32", H);
   if (E < 1 || E > MOE_MAX_GATE_EXPERTS)
@@ -755,21 +761,75 @@ moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, c
   if (k < 1 || k > MOE_MAX_TOPK || k > E)
     return fail(MOE_ERR_INVALID_ARG, "k %d outside 1..min(%d, E)", k, MOE_MAX_TOPK);
   if (T == 0) return MOE_OK;
-  if (!x || !wr || !workspace || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "x, wr, workspace, ids or w is NULL");
-  if (!aligned16(x) || !aligned16(wr) || !aligned16(workspace))
+  if (!x || !wr || (need_ws && !workspace) || !ids || !w)
+    return fail(MOE_ERR_INVALID_ARG, "x, wr, workspace, ids or w is NULL");
+  if (!aligned16(x) || !aligned16(wr) || (need_ws && !aligned16(workspace)))
     return fail(MOE_ERR_INVALID_ARG, "x, wr and workspace must be 16-byte aligned");
   if (((uintptr_t)ids | (uintptr_t)w | (uintptr_t)logits) & 3u)
     return fail(MOE_ERR_INVALID_ARG, "logits, ids and w must be 4-byte aligned");
-  const size_t need = moe_gate_workspace_bytes(T, H, E);
-  if (workspace_bytes < need)
-    return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes; this shape needs %zu", workspace_bytes, need);
+  return MOE_OK;
+}
+
+// The two launches of the fused gate, partial sums in `part` (ks x T x E fp32).
+static moe_status gate_launch(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, float* part,
+                              float* logits, int32_t* ids, float* w, hipStream_t stream) {
   const int ks = gate_split(T, H, E);
-  float* part = static_cast<float*>(workspace);
   RouterSplitArgs ra{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), part, T, H, E, ks};
   HIP_TRY(launch_router_split(ra, stream));
   TopkArgs ta{part, logits, ids, w, T, E, k, ks};
   HIP_TRY(launch_topk(ta, stream));
   return MOE_OK;
+}
+
+// Scratch of moe_gate_noalloc: one array per GPU, in the library's device code, holding
+// the router's partial sums.  In host code `scratch` only names the symbol; its device
+// address (a different one on every GPU) comes from hipGetSymbolAddress, looked up once
+// per device on the first call there and kept in g_scratch_dev.
+static __device__ __align__(256) uint8_t scratch[MOE_GATE_NOALLOC_MAX_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices] = {};
+
+static moe_status scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_gate_noalloc(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, float* logits,
+                            int32_t* ids, float* w, hipStream_t stream) {
+  moe_status st = gate_check(T, H, E, k, x, wr, nullptr, false, logits, ids, w);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = moe_gate_workspace_bytes(T, H, E);
+  if (need > MOE_GATE_NOALLOC_MAX_BYTES)
+    return fail(MOE_ERR_INVALID_ARG, "this shape needs %zu bytes of scratch; moe_gate_noalloc holds %u", need,
+                (unsigned)MOE_GATE_NOALLOC_MAX_BYTES);
+  void* part = nullptr;
+  st = scratch_address(&part);
+  if (st != MOE_OK) return st;
+  return gate_launch(T, H, E, k, x, wr, static_cast<float*>(part), logits, ids, w, stream);
+}
+
+moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, void* workspace,
+                    size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream) {
+  moe_status st = gate_check(T, H, E, k, x, wr, workspace, true, logits, ids, w);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = moe_gate_workspace_bytes(T, H, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes; this shape needs %zu", workspace_bytes, need);
+  return gate_launch(T, H, E, k, x, wr, static_cast<float*>(workspace), logits, ids, w, stream);
 }
 
 int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream_t stream) {

@@ -329,6 +329,23 @@ moe_status moe_gate(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, c
                     size_t workspace_bytes, float* logits, int32_t* ids, float* w, hipStream_t stream);
 
 /*
+ * moe_gate_noalloc: moe_gate without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The router's partial sums go to a
+ * fixed scratch array of MOE_GATE_NOALLOC_MAX_BYTES in the library's device code (one per
+ * GPU, held until the process ends); a shape whose moe_gate_workspace_bytes exceeds it
+ * (beyond 4096 tokens at 256 experts) returns MOE_ERR_INVALID_ARG before any work is
+ * enqueued.  The first call on a device looks up that device's copy of the array (no
+ * allocation).  Results are bit-identical to moe_gate's for the same arguments.  Every
+ * call on one GPU uses the same array: calls that overlap on one GPU (different streams
+ * with no order between them, or different threads) race and give undefined results.
+ * Other arguments and rules as for moe_gate.
+ */
+#define MOE_GATE_NOALLOC_MAX_BYTES (4u << 20)
+moe_status moe_gate_noalloc(int32_t T, int32_t H, int32_t E, int32_t k, const void* x, const void* wr, float* logits,
+                            int32_t* ids, float* w, hipStream_t stream);
+
+/*
  * Measurement aid, not part of the layer: launches `blocks` workgroups that issue only
  * FP8 MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4, operands in registers, no memory
  * traffic) `iters` times per chain, and returns the flops the launch performs (-1 on

@@ -159,3 +159,23 @@ def test_mfma_dot_rejects_bad_arguments(lib):
     assert lib.moe_mfma_dot16x16(binding.MOE_FP8_E4M3, None, _A16, _A16, None) == inv
     assert lib.moe_mfma_dot16x16(binding.MOE_FP4_E2M1, _A16, None, _A16, None) == inv
     assert lib.moe_mfma_dot16x16(binding.MOE_FP8_E4M3, _A16, _A16, ctypes.c_void_p(0x10002), None) == inv
+
+
+@pytest.mark.parametrize("T,H,E,k,needle", [
+    (4097, 7168, 256, 8, "scratch"),   # 4097 x 256 fp32 partial sums exceed the 4 MiB array
+    (-1, 256, 8, 2, "T"),
+    (4, 100, 8, 2, "H"),
+    (4, 256, 300, 2, "E"),
+    (4, 256, 8, 9, "k"),
+])
+def test_noalloc_gate_rejects_bad_arguments(lib, T, H, E, k, needle):
+    st = lib.moe_gate_noalloc(T, H, E, k, _A16, _A16, None, _A16, _A16, None)
+    assert st == binding.MOE_ERR_INVALID_ARG
+    assert needle in lib.moe_last_error_message().decode()
+
+
+def test_noalloc_gate_null_and_empty(lib):
+    assert lib.moe_gate_noalloc(0, 256, 8, 2, None, None, None, None, None, None) == binding.MOE_OK
+    assert lib.moe_gate_noalloc(4, 256, 8, 2, None, _A16, None, _A16, _A16, None) == binding.MOE_ERR_INVALID_ARG
+    # the largest shape it takes: 4096 tokens x 256 experts (no K split) fill the array exactly
+    assert lib.moe_gate_workspace_bytes(4096, 7168, 256) == 4 << 20
