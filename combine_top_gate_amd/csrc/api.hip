@@ -35,6 +35,7 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // persistent GEMM: ~0.2 s of s_sleep
 constexpr uint32_t kSentinelSpin = 1u << 20;  // SENTINEL GEMM1: polls before a wait gives up
 constexpr int kXcds = 8;                     // CU mask bits are spread over the XCDs
 constexpr double kTiledRows = 192.0;       // mean rows per expert from which the tiled GEMM runs
+constexpr int kMaxDelayUs = 10000;          // SENTINEL dispatch delay cap, far below the wait limit
 
 }  // namespace
 
@@ -68,6 +69,8 @@ struct moe_ctx {
   uint32_t epoch = 0;
   uint32_t spin_limit = kSentinelSpin;
   int opt_stall = 0;
+  int opt_poison = 0;           // fill windows, h and y with NaN codes before each layer call
+  uint32_t delay_ticks = 0;     // SENTINEL dispatch delay (100 MHz ticks), a test aid
   // options
   int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0, opt_tiled_m32 = 0;
   // state of the last dispatch
@@ -256,8 +259,8 @@ moe_status moe_destroy(moe_ctx* c) {
 // Validates the dispatch arguments and fills `da` (nothing is launched; T_s == 0 leaves
 // da.T_s = 0).  publish: SENTINEL flags for this call's epoch; blocks: workgroups
 // the chunks should spread over.
-static moe_status dispatch_prepare(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
-                                   const int32_t* ids, bool publish, int blocks, DispatchArgs& da) {
+static moe_status check_dispatch(const moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                                 const int32_t* ids) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
   const moe_config& cf = c->cfg;
   if (T_s < 0 || T_s > cf.max_tokens)
@@ -273,6 +276,15 @@ static moe_status dispatch_prepare(moe_ctx* c, int32_t T_s, const void* const* x
         return fail(MOE_ERR_INVALID_ARG, "x_scale[%d] is NULL or misaligned", s);
     }
   }
+  return MOE_OK;
+}
+
+static moe_status dispatch_prepare(moe_ctx* c, int32_t T_s, const void* const* x, const float* const* x_scale,
+                                   const int32_t* ids, bool publish, int blocks, DispatchArgs& da) {
+  const moe_status st = check_dispatch(c, T_s, x, x_scale, ids);
+  if (st != MOE_OK) return st;
+  const moe_config& cf = c->cfg;
+  const bool fp8 = cf.act == MOE_FP8_E4M3;
   SrcPtrs src{};
   for (int s = 0; s < cf.n_src && T_s > 0; ++s) {
     src.x[s] = static_cast<const uint8_t*>(x[s]);
@@ -303,6 +315,7 @@ static moe_status dispatch_prepare(moe_ctx* c, int32_t T_s, const void* const* x
     da.dflag = c->sync + MOE_MAX_SRC;
     da.arrive = c->sync + 2 * MOE_MAX_SRC;
     da.epoch = c->epoch;
+    da.delay_ticks = c->delay_ticks;
   }
   return MOE_OK;
 }
@@ -339,17 +352,11 @@ static bool sentinel_applies(const moe_ctx* c, int T_s) {
   return !use_tiled(c, dims(c, T_s));
 }
 
-// sn: SENTINEL -- GEMM1 polls the dispatch's flags.  fused != null: the dispatch chunks
-// run in the GEMM1 launch itself, on `stream`; otherwise GEMM1 runs on the compute
-// stream and GEMM2 joins both streams back into `stream`.
-static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed, bool sn = false,
-                             const DispatchArgs* fused = nullptr) {
+// The weight pointers of a call (nothing is launched).
+static moe_status check_weights(const moe_ctx* c, const moe_weights* w) {
   const moe_config& cf = c->cfg;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
-  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
-  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1, a16 = cf.act == MOE_BF16;
-  // the kernel variant: FP8 or MXFP4 weights with FP8 activations, or W4A16
-  const int wf = a16 ? kFmtW4A16 : cf.weight;
+  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1;
   if (!w->w13 || !w->w2 || (!f32 && (!w->s13 || !w->s2)))
     return fail(MOE_ERR_INVALID_ARG, "routed expert weight or scale pointer is NULL");
   if (!aligned16(w->w13) || !aligned16(w->w2)) return fail(MOE_ERR_INVALID_ARG, "weights not 16-byte aligned");
@@ -362,6 +369,41 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     if (!aligned16(w->sh_w13) || !aligned16(w->sh_w2))
       return fail(MOE_ERR_INVALID_ARG, "shared weights not 16-byte aligned");
   }
+  return MOE_OK;
+}
+
+// Test aid (MOE_OPT_POISON): windows, their scales, h, its scales and y filled with NaN
+// codes of their formats, so that a kernel reading a row the call has not written
+// produces NaN.
+static moe_status poison(moe_ctx* c, hipStream_t stream) {
+  const moe_config& cf = c->cfg;
+  const bool f32 = cf.act == MOE_F32, fp8 = cf.act == MOE_FP8_E4M3;
+  const uint32_t act = f32 ? 0x7FC00000u : fp8 ? 0x7F7F7F7Fu : 0x7FC07FC0u;  // e4m3 NaN 0x7F, bf16 NaN
+  const uint32_t out = f32 ? 0x7FC00000u : 0x7FC07FC0u;
+  const int H = cf.hidden;
+  HIP_TRY(launch_fill32(c->win, (size_t)c->R_cap * c->row_bytes, act, stream));
+  HIP_TRY(launch_fill32(c->h, (size_t)c->rows_cap * c->hstride * c->act_bytes, act, stream));
+  HIP_TRY(launch_fill32(c->y, (size_t)c->rows_cap * H * (f32 ? 4 : 2), out, stream));
+  if (fp8) {
+    HIP_TRY(launch_fill32(c->wsc, (size_t)c->R_cap * (H / 128) * 4, 0x7FC00000u, stream));
+    HIP_TRY(launch_fill32(c->hs, (size_t)c->rows_cap * (c->hstride / 128) * 4, 0x7FC00000u, stream));
+  }
+  return MOE_OK;
+}
+
+// sn: SENTINEL -- GEMM1 polls the dispatch's flags.  fused != null: the dispatch chunks
+// run in the GEMM1 launch itself, on `stream`; otherwise GEMM1 runs on the compute
+// stream and GEMM2 joins both streams back into `stream`.
+static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed, bool sn = false,
+                             const DispatchArgs* fused = nullptr) {
+  const moe_config& cf = c->cfg;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
+  const bool f32 = cf.act == MOE_F32, fp4 = cf.weight == MOE_FP4_E2M1, a16 = cf.act == MOE_BF16;
+  // the kernel variant: FP8 or MXFP4 weights with FP8 activations, or W4A16
+  const int wf = a16 ? kFmtW4A16 : cf.weight;
+  const moe_status wst = check_weights(c, w);
+  if (wst != MOE_OK) return wst;
   if (c->T_s == 0) {
     if (timed) { record(c, 2, stream); }
     return MOE_OK;
@@ -513,8 +555,12 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
                      const int32_t* ids, const float* topk_w, const moe_weights* w, void* out,
                      hipStream_t stream) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
-  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  moe_status st = check_weights(c, w);
+  if (st != MOE_OK) return st;
   if (T_s > 0 && (!topk_w || !out)) return fail(MOE_ERR_INVALID_ARG, "topk_w or out is NULL");
+  if (T_s > 0 && !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "out is not 16-byte aligned");
+  st = check_dispatch(c, T_s, x, x_scale, ids);  // every argument is checked before anything is enqueued
+  if (st != MOE_OK) return st;
   const bool timed = c->timing_n < c->timing_cap;
   const bool sn = sentinel_applies(c, T_s);
   if (sn || timed) {
@@ -525,8 +571,11 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
       return fail(MOE_ERR_INVALID_ARG, "%s cannot be captured into a graph",
                   sn ? "a SENTINEL layer call (per-call epoch)" : "a timed layer call");
   }
+  if (c->opt_poison && T_s > 0) {
+    st = poison(c, stream);
+    if (st != MOE_OK) return st;
+  }
   if (timed) record(c, 0, stream);
-  moe_status st;
   DispatchArgs fused;
   const bool use_fused = sn && c->dispatch_cus == 0;
   if (use_fused) {
@@ -706,6 +755,21 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
     case MOE_OPT_TILED_MFMA:
       if (v != 0 && v != 1) break;
       c->opt_tiled_m32 = v;
+      return MOE_OK;
+    case MOE_OPT_POISON:
+      if (v != 0 && v != 1) break;
+      c->opt_poison = v;
+      return MOE_OK;
+    case MOE_OPT_EPOCH: {
+      // the flags may hold any earlier epoch: clear them, with the device idle
+      HIP_TRY(hipDeviceSynchronize());
+      HIP_TRY(hipMemset(c->sync, 0, 3 * MOE_MAX_SRC * 4));
+      c->epoch = (uint32_t)v;
+      return MOE_OK;
+    }
+    case MOE_OPT_DISPATCH_DELAY:
+      if (v < 0 || v > kMaxDelayUs) break;
+      c->delay_ticks = (uint32_t)v * 100u;  // the real-time counter runs at 100 MHz
       return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);

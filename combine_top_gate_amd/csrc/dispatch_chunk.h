@@ -198,6 +198,14 @@ __device__ __forceinline__ void dispatch_chunk_u(const DispatchArgs& a, int s, i
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.rflag + s, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (a.delay_ticks) {
+    // test aid: hold the window rows back, so GEMM1 workgroups that have seen the counts
+    // must wait for the rows (bounded: the host caps the delay far below the wait limit)
+    // (each pass sleeps 512 clocks, over 20 ticks: the pass count ends the loop too)
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + a.delay_ticks;
+    for (uint32_t it = 0; it < a.delay_ticks && __builtin_amdgcn_s_memrealtime() < t_end; ++it)
+      __builtin_amdgcn_s_sleep(8);
+  }
 
   // copy: each token row is read once as 16-byte vectors and written to its k rows
   if (tid < work) dispatch_copy_store<U>(a, work, tid, first, s_dst);

@@ -27,6 +27,8 @@ struct DispatchArgs {
   uint32_t* dflag;     // [S] every window row of the source written
   uint32_t* arrive;    // [S] arrival counters (zero between calls)
   uint32_t epoch;
+  uint32_t delay_ticks;  // SENTINEL test aid: each chunk waits this many 100 MHz ticks after
+                         // publishing the counts, before it writes its window rows (0 = none)
 };
 int dispatch_tokens_per_block(int T_s, int k, int blocks_wanted, int S);
 int dispatch_chunks(const DispatchArgs& a);  // workgroups per source
@@ -157,6 +159,10 @@ struct TopkArgs {
   int T, E, k, ks;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+// ---- buffer fill (fill.hip) ------------------------------------------------------
+// p 16-byte aligned; bytes a multiple of 4 (the remainder is not written).
+hipError_t launch_fill32(void* p, size_t bytes, uint32_t pattern, hipStream_t st);
 
 // ---- measurement aid ----------------------------------------------------------
 hipError_t launch_mfma_fp8_probe(float* sink, int blocks, int iters, hipStream_t st);

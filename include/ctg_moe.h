@@ -64,8 +64,12 @@
  *   - Block scales are fp32 multipliers (real value = code value * scale):
  *     activations 1x128 along the hidden dimension; FP8 weights 128x128 over
  *     (output row, input column); MXFP4 weights e8m0 per 1x32 along the input.
- *   - All calls are asynchronous on the given stream (0 = the null stream) and
- *     allocate nothing except moe_create.  A context is not thread-safe; calls on
+ *   - The layer calls (moe_dispatch, moe_grouped_gemm, moe_combine, moe_combine_fp8,
+ *     moe_layer) and the gate calls are asynchronous on the given stream (0 = the null
+ *     stream) and allocate nothing; moe_get_routing and moe_copy_buffer enqueue copies.
+ *     Allocation happens only in moe_create (the workspace) and moe_set_timing (its
+ *     events); moe_last_device_error, moe_read_timing, moe_set_timing and the
+ *     MOE_OPT_EPOCH option wait for the device.  A context is not thread-safe; calls on
  *     one context must be issued on one stream (or be ordered by the caller).
  *   - Arguments are validated on the host before any work is enqueued; a
  *     non-OK status means nothing was enqueued, and moe_last_error_message()
@@ -273,6 +277,17 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *                            1: 32x32x64, the two 64-deep halves of a 128-deep scale block
  *                            chained before one promotion (results agree with 0 to fp32
  *                            rounding of the block sums, not bit for bit).
+ * Test aids for the handshake and the reuse of the workspace without a clean pass:
+ *   MOE_OPT_POISON           1: every moe_layer call first fills the windows, their scales,
+ *                            h, its scales and y (all rows of the capacity) with NaN codes
+ *                            of their formats (a kernel, enqueued on the call's stream), so
+ *                            that reading a row the call has not written shows; 0: off.
+ *   MOE_OPT_EPOCH            sets the SENTINEL epoch counter to (uint32_t)value (the next
+ *                            call uses the value after it, skipping 0) and clears the flags;
+ *                            waits for the device.  For calls across the counter's wrap.
+ *   MOE_OPT_DISPATCH_DELAY   SENTINEL: every dispatch chunk waits this many microseconds
+ *                            (0..10000) after publishing the counts and before writing its
+ *                            window rows, so GEMM1 workgroups wait on the row flags; 0: off.
  * Unknown options or values return MOE_ERR_INVALID_ARG.
  */
 typedef enum {
@@ -282,7 +297,10 @@ typedef enum {
   MOE_OPT_TILED_GEMM = 3,
   MOE_OPT_SENTINEL_SPIN = 4,
   MOE_OPT_SENTINEL_STALL = 5,
-  MOE_OPT_TILED_MFMA = 6
+  MOE_OPT_TILED_MFMA = 6,
+  MOE_OPT_POISON = 7,
+  MOE_OPT_EPOCH = 8,
+  MOE_OPT_DISPATCH_DELAY = 9
 } moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 

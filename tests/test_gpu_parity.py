@@ -200,20 +200,6 @@ def test_persistent_gemm_matches_oracle(name, over, queue):
     check(moe, inp, d)
 
 
-def test_many_back_to_back_calls_reuse_scheduler_state():
-    """The persistent GEMM resets its queues and counters itself: 60 calls, no clean pass."""
-    inp = synth.make_inputs("decode128_fp8", S=8, T_s=4, H=1024, I=512, E=32, k=4, seed=55)
-    moe, d = run(inp, packed=True)
-    ref = d.out.clone()
-    outs = []
-    for _ in range(60):
-        moe.run(d)
-        outs.append(d.out.clone())
-    torch.cuda.synchronize()
-    assert all(torch.equal(ref, o) for o in outs)
-    assert moe.device_error() == 0
-
-
 SENTINEL_CASES = [
     ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=71), 0),
     ("decode256_mxfp4_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=384, seed=72), 0),
@@ -295,7 +281,9 @@ def test_invalid_options():
     moe = binding.Moe.for_inputs(inp)
     for opt, val in [(binding.MOE_OPT_TOKEN_TILES, 1), (binding.MOE_OPT_TOKEN_TILES, 7), (binding.MOE_OPT_QUEUE, 3),
                      (binding.MOE_OPT_PERSISTENT_GEMM, 2), (binding.MOE_OPT_SENTINEL_SPIN, -1),
-                     (binding.MOE_OPT_SENTINEL_STALL, 2), (binding.MOE_OPT_TILED_MFMA, 2), (9, 0)]:
+                     (binding.MOE_OPT_SENTINEL_STALL, 2), (binding.MOE_OPT_TILED_MFMA, 2),
+                     (binding.MOE_OPT_POISON, 2), (binding.MOE_OPT_DISPATCH_DELAY, -1),
+                     (binding.MOE_OPT_DISPATCH_DELAY, 10001), (10, 0)]:
         with pytest.raises(binding.MoeError):
             moe.set_option(opt, val)
 
