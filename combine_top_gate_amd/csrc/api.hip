@@ -579,10 +579,12 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
   DispatchArgs fused;
   const bool use_fused = sn && c->dispatch_cus == 0;
   if (use_fused) {
-    // the dispatch chunks become the first workgroups of the GEMM1 launch
+    // the dispatch chunks run in the prologue of the GEMM1 launch's first workgroups
+    // (at most one chunk per CU's worth of workgroups)
     c->epoch = c->epoch + 1 ? c->epoch + 1 : 1;  // 0 (the flags' initial value) is never an epoch
-    st = dispatch_prepare(c, T_s, x, x_scale, ids, true, 2 * c->n_cu, fused);
+    st = dispatch_prepare(c, T_s, x, x_scale, ids, true, c->n_cu / 2, fused);
     if (st != MOE_OK) return st;
+    fused.rflag = nullptr;  // the GEMM1 workgroups wait for the rows flags only
     if (timed) record(c, 1, stream);
   } else if (sn) {
     // fork: dispatch and GEMM1 start together on their CU sets once `stream` is here

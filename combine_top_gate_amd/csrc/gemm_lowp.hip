@@ -483,10 +483,12 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, const SegTable& t,
 }
 
 // ------------------------------------------------------------------ GEMM1
+// w0: the pass's first weight slab; issued here unless `issued` (the caller issued it
+// earlier, so that its latency overlaps the caller's own work).
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
                                            int g, int nb, int M, int m0, float (*s_amax)[kMaxTok], float* s_tsc,
-                                           uint8_t* s_tok) {
+                                           uint8_t* s_tok, WSlab<WFMT>& w0, bool issued) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -495,8 +497,7 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
   const float* tsc[NT];
   int orow[NT];
   TokStage<NT, A16> ts;
-  WSlab<WFMT> w0;
-  load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
+  if (!issued) load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
   pass_rows<NT, true, A16>(p, t, g, M, m0, tsc, orow);
   stage_rows<NT, true, A16>(p, t, g, M, m0, ts);
@@ -567,9 +568,28 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
 
 // One GEMM1 work item: column block nb (128 gate + 128 up rows) of expert group g, over
 // all of the group's rows.  Every thread of the workgroup calls it.
-template <int NTMAX, int WFMT, bool PACKED>
+// prologue (SENTINEL, dispatch fused into this launch): the item's first weight slab and
+// its weight scales are issued, then this workgroup runs dispatch chunk `chunk` of `da`
+// (if chunk >= 0; every chunk of the dispatch is some workgroup's), and only then does it
+// wait for the counts and rows its expert needs -- so the dispatch runs on every CU at
+// the start of the launch, under the latency of the first weight loads.
+struct NoPrologue {
+  static constexpr bool kOn = false;
+  __device__ void operator()() const {}
+};
+struct DispatchPrologue {
+  static constexpr bool kOn = true;
+  const DispatchArgs& da;
+  int chunk, chunks;  // chunk < 0: none for this workgroup
+  __device__ void operator()() const {
+    if (chunk >= 0) dispatch_chunk(da, chunk / chunks, chunk % chunks, chunks, *reinterpret_cast<DispatchSmem*>(g_lds));
+  }
+};
+
+template <int NTMAX, int WFMT, bool PACKED, class Prologue = NoPrologue>
 __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item, float (*s_amax)[kMaxTok],
-                                           float* s_tsc, uint8_t* s_tok, SegTable& seg) {
+                                           float* s_tsc, uint8_t* s_tok, SegTable& seg,
+                                           const Prologue& prologue = Prologue{}) {
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -578,18 +598,12 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
   const int inter = shared ? d.Ish : d.I;
   // the shared expert reads the source buffers, so only routed groups wait
   const bool sentinel = p.rflag != nullptr && !shared;
-  if (sentinel && !sentinel_wait(p, p.rflag, nullptr)) return;
-  const int M = load_segments(p, g, seg);
   // the shared expert's rows are split into chunks, each its own work item
-  int mb = 0, me = M;
+  int shc = 0;
   if (shared) {
-    const int chunk = nb % p.sh_chunks;
+    shc = nb % p.sh_chunks;
     nb /= p.sh_chunks;
-    mb = chunk * p.sh_chunk_rows;
-    me = min(M, mb + p.sh_chunk_rows);
   }
-  if (M == 0) return;  // no rows: no weight traffic (uniform over the workgroup)
-
   const int K = d.H, KB = K >> 7;
   constexpr bool FP4 = kFp4W<WFMT>;
   constexpr int SF = WeightFmt<WFMT>::kStore;
@@ -610,6 +624,12 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
       if constexpr (FP4) ws.erow[mt] = WSb + (int64_t)(rows[mt] + r16) * (K >> 5) + g4;
     }
   }
+  WSlab<WFMT> w0;
+  constexpr bool pro = Prologue::kOn;
+  if constexpr (pro) {
+    load_wslab(w0, ws, 0);  // in flight across the dispatch chunk and the waits
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (!FP4) {
     const float* FS = reinterpret_cast<const float*>(WSb);
     // gate rows: block nb; up rows: block I/128 + nb
@@ -617,41 +637,64 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) ws.fsel[mt] = mt >> 1;
   }
-  // the weight scales are in flight while this group's window rows are awaited
-  if (sentinel && !sentinel_wait(p, p.dflag, &seg)) return;
+  if constexpr (pro) {
+    prologue();
+    __syncthreads();  // the dispatch's LDS is the passes' LDS
+  }
+  // prologue form: one wait, for every source's rows (their last writer also published
+  // the counts, so one acquire covers both); else the counts first, then the rows of the
+  // sources that hold rows of this group, with the weight scales in flight meanwhile
+  if (sentinel && !sentinel_wait(p, pro ? p.dflag : p.rflag, nullptr)) return;
+  const int M = load_segments(p, g, seg);
+  int mb = 0, me = M;
+  if (shared) {
+    mb = shc * p.sh_chunk_rows;
+    me = min(M, mb + p.sh_chunk_rows);
+  }
+  if (M == 0) return;  // no rows: no weight traffic (uniform over the workgroup)
+  if (!pro && sentinel && !sentinel_wait(p, p.dflag, &seg)) return;
 
   for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
+    const bool issued = pro && m0 == mb;
     switch (nt) {
-      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
-      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
-      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
-      case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
-      case 5: if constexpr (NTMAX >= 5) gemm1_pass<WFMT, PACKED, 5>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
-      default: if constexpr (NTMAX >= 6) gemm1_pass<WFMT, PACKED, 6>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok); break;
+      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      case 5: if constexpr (NTMAX >= 5) gemm1_pass<WFMT, PACKED, 5>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      default: if constexpr (NTMAX >= 6) gemm1_pass<WFMT, PACKED, 6>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
     }
   }
 }
 
-// ndisp > 0 (fused SENTINEL launch): workgroups 0 .. ndisp-1 run the dispatch chunks
-// (da, `chunks` per source; a multiple of 8 so every XCD keeps its b % 8 blocks) and
-// the work items follow.  A GPU places a launch's workgroups in index order, so every
-// dispatch chunk is resident before any work item that waits for it.
-template <int NTMAX, int WFMT, bool PACKED>
-__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs da, int ndisp, int chunks) {
+// nchunks > 0 (SENTINEL, dispatch fused into this launch): workgroup b < nchunks runs
+// dispatch chunk b (of `chunks` per source) in its prologue (gemm1_item); workgroups past
+// the last work item (when chunks outnumber items) run only their chunk.  Every chunk is
+// run by one of the lowest-numbered workgroups, which a GPU places first, and a chunk
+// never waits for anything, so every flag a workgroup waits on is published by a
+// workgroup that is already running.
+template <int NTMAX, int WFMT, bool PACKED, bool FUSED>
+__global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs da, int nchunks, int chunks) {
   __shared__ float s_amax[4][kMaxTok];
   __shared__ SegTable seg;
   float* s_tsc = reinterpret_cast<float*>(g_lds);
   uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.H >> 7, NTMAX, kA16<WFMT>);
-  if ((int)blockIdx.x < ndisp) {
-    // the launch sizes the dynamic LDS to hold a DispatchSmem as well
-    const int b = blockIdx.x;
-    if (b < da.S * chunks) dispatch_chunk(da, b / chunks, b % chunks, chunks, *reinterpret_cast<DispatchSmem*>(g_lds));
-    return;
+  const int b = blockIdx.x;
+  const int items = p.d.E * (p.d.I >> 7) + (p.d.Ish >> 7) * p.sh_chunks;
+  if constexpr (FUSED) {
+    if (b >= items) {
+      if (b < nchunks) dispatch_chunk(da, b / chunks, b % chunks, chunks, *reinterpret_cast<DispatchSmem*>(g_lds));
+      return;
+    }
   }
   int g, nb;
-  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, (int)blockIdx.x - ndisp, g, nb);
-  gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg);
+  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, b, g, nb);
+  if constexpr (FUSED)
+    gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg,
+                                    DispatchPrologue{da, b < nchunks ? b : -1, chunks});
+  else
+    gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg);
 }
 
 // ------------------------------------------------------------------ GEMM2
@@ -851,27 +894,40 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
 template <int WFMT, bool PACKED>
 hipError_t launch1(const GemmArgs& a, int nt, const DispatchArgs* fused, hipStream_t st) {
   DispatchArgs da{};
-  int ndisp = 0, chunks = 0;
+  int nchunks = 0, chunks = 0;
   if (fused) {
     da = *fused;
     chunks = dispatch_chunks(da);
-    ndisp = (da.S * chunks + 7) / 8 * 8;
+    nchunks = da.S * chunks;
   }
-  const dim3 grid(ndisp + a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks), block(256);
+  const int items = a.d.E * (a.d.I >> 7) + (a.d.Ish >> 7) * a.sh_chunks;
+  const dim3 grid(std::max(items, nchunks)), block(256);
   const int KB = a.d.H >> 7;
   auto lds = [&](int ntmax) {
     const int b = lds_bytes(KB, ntmax, kA16<WFMT>);
-    return (size_t)(ndisp && b < (int)sizeof(DispatchSmem) ? (int)sizeof(DispatchSmem) : b);
+    return (size_t)(nchunks && b < (int)sizeof(DispatchSmem) ? (int)sizeof(DispatchSmem) : b);
   };
-  if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED>), grid, block, lds(2), st, a, da, ndisp, chunks);
-  else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED>), grid, block, lds(3), st, a, da, ndisp, chunks);
-  else if (nt == 4 || !kFp4W<WFMT>)
-    hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED>), grid, block, lds(4), st, a, da, ndisp, chunks);
-  else
-    hipLaunchKernelGGL((k_gemm1_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED>), grid, block, lds(5), st, a, da,
-                       ndisp, chunks);
+  if (nchunks) {
+    if (nt <= 2)
+      hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED, true>), grid, block, lds(2), st, a, da, nchunks, chunks);
+    else if (nt == 3)
+      hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED, true>), grid, block, lds(3), st, a, da, nchunks, chunks);
+    else if (nt == 4 || !kFp4W<WFMT>)
+      hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED, true>), grid, block, lds(4), st, a, da, nchunks, chunks);
+    else
+      hipLaunchKernelGGL((k_gemm1_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED, true>), grid, block, lds(5), st,
+                         a, da, nchunks, chunks);
+  } else {
+    if (nt <= 2)
+      hipLaunchKernelGGL((k_gemm1_lowp<2, WFMT, PACKED, false>), grid, block, lds(2), st, a, da, 0, 0);
+    else if (nt == 3)
+      hipLaunchKernelGGL((k_gemm1_lowp<3, WFMT, PACKED, false>), grid, block, lds(3), st, a, da, 0, 0);
+    else if (nt == 4 || !kFp4W<WFMT>)
+      hipLaunchKernelGGL((k_gemm1_lowp<4, WFMT, PACKED, false>), grid, block, lds(4), st, a, da, 0, 0);
+    else
+      hipLaunchKernelGGL((k_gemm1_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED, false>), grid, block, lds(5),
+                         st, a, da, 0, 0);
+  }
   return hipGetLastError();
 }
 

@@ -43,9 +43,10 @@
  * Green Contexts", section "Three-Node CUDA Graph and token-ring Handshake").
  * Epoch tags grow monotonically, so no clean pass is needed between calls.
  * Two forms, chosen by dispatch_cus:
- *   0   the dispatch chunks are the first workgroups of the GEMM1 launch itself
- *       (one queue; workgroups are placed in index order, so a waiting GEMM
- *       workgroup never holds back the chunk it waits for);
+ *   0   the dispatch runs inside the GEMM1 launch itself: each of its first
+ *       workgroups issues its first weight loads, runs one dispatch chunk, and only
+ *       then waits (one queue; workgroups are placed in index order, and a chunk
+ *       waits for nothing, so every flag awaited is published by a running workgroup);
  *   >0  the dispatch kernel runs on a stream restricted to dispatch_cus CUs and
  *       GEMM1 on a stream holding the other CUs (the partition of the "GC-MoE"
  *       pages); GEMM2 and the combine run on the caller's stream after both
