@@ -97,6 +97,13 @@ __device__ __forceinline__ void wait_barrier() {
 
 constexpr int kStages = 2;  // LDS ring depth: loads run kStages - 1 slabs ahead
 
+// Where an expert's rows live: source s's bucket holds rows pre[s] .. pre[s+1]-1 of the
+// expert window, starting at window row row0[s] (see gemm_lowp.hip SegTable).
+struct Segs {
+  int pre[MOE_MAX_SRC + 1];
+  int row0[MOE_MAX_SRC];
+};
+
 struct __align__(16) Tiles {
   uint8_t a[kStages][BM * kStride];
   uint8_t w[kStages][BN * kStride];
@@ -104,8 +111,7 @@ struct __align__(16) Tiles {
   float sw[kStages][64];    // weight scales of the staged slab (two 128-row blocks) in [0..1]
   float sdummy[64];         // where the idle lanes' scale loads go
   float amax[4][BM];        // GEMM1: per weight quarter, per token row
-  int pre[MOE_MAX_SRC + 1]; // expert row segments (see gemm_lowp.hip SegTable)
-  int row0[MOE_MAX_SRC];
+  Segs seg[2];              // expert row segments of the current and the next item
   int item;
 };
 
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256) void k_plan(TiledArgs t) {
   if (threadIdx.x < 2 * kXcds) t.plan[kPlanCtr + threadIdx.x] = 0;
 }
 
-__device__ __forceinline__ void segments(const GemmArgs& p, int g, Tiles& T) {
+__device__ __forceinline__ void segments(const GemmArgs& p, int g, Segs& T) {
   const BatchDims& d = p.d;
   if (threadIdx.x < 64 && g < d.E) {
     const int s = threadIdx.x;
@@ -170,7 +176,7 @@ __device__ __forceinline__ void segments(const GemmArgs& p, int g, Tiles& T) {
   }
 }
 
-__device__ __forceinline__ int seg_row(const Tiles& T, int S, int m) {
+__device__ __forceinline__ int seg_row(const Segs& T, int S, int m) {
   int s = 0;
   while (s + 1 < S && m >= T.pre[s + 1]) ++s;
   return T.row0[s] + (m - T.pre[s]);
@@ -180,24 +186,28 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // One item: token tile [m0, m0 + BM) of group g (M rows), weight block nb.  M32: the K
 // loop on v_mfma_scale_f32_32x32x64_f8f6f4 instead of 16x16x128 (see below).
-template <bool GEMM1, bool M32>
-__device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles& T, bool t_packed) {
+// This thread's DMA sources for one work item (token tile [m0, m0 + BM) of group g with M
+// rows, weight block nb).  Instruction i of wave w fills the 1 KB at 16 * ((w * n + i) * 64
+// + lane) of a stage buffer: chunk p = (w * n + i) * 64 + lane is physical chunk p % 8 of
+// row p / 8, which holds that row's logical chunk (p % 8) ^ ((row >> 1) & 7) (the swizzle
+// of swz()).
+struct TileSrc {
+  const uint8_t* a[kALd];
+  const uint8_t* w[kWLd];
+  const float* s;
+  int64_t wstep;
+};
+
+template <bool GEMM1>
+__device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int m0, int nb, const Segs& sg,
+                                            bool t_packed) {
   const BatchDims& d = p.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 2, wn = wave & 3;  // token half, weight quarter
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
   const int K = GEMM1 ? d.H : inter;
   const int KB = K >> 7;
-  const int seg = d.T_s * d.k;
-  (void)seg;
-
-  // ---- this thread's DMA sources.  Instruction i of wave w fills the 1 KB at
-  // 16 * ((w * n + i) * 64 + lane) of a stage buffer: chunk p = (w * n + i) * 64 + lane
-  // is physical chunk p % 8 of row p / 8, which holds that row's logical chunk
-  // (p % 8) ^ ((row >> 1) & 7) (the swizzle of swz()).
-  const uint8_t* asrc[kALd];
+  TileSrc src;
 #pragma unroll
   for (int i = 0; i < kALd; ++i) {
     const int q = (wave * kALd + i) * 64 + lane;
@@ -209,10 +219,10 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       const int s = m / d.T_s, tt = m - s * d.T_s;
       rowp = p.src.x[s] + (int64_t)tt * d.H;
     } else {
-      const int wr = shared ? d.R + m : seg_row(T, d.S, m);
+      const int wr = shared ? d.R + m : seg_row(sg, d.S, m);
       rowp = p.a + (int64_t)wr * (GEMM1 ? d.H : d.hstride);
     }
-    asrc[i] = rowp + c * 16;
+    src.a[i] = rowp + c * 16;
   }
   const uint8_t* W = shared ? p.w_sh : p.w + (int64_t)g * p.w_stride;
   const float* WS = static_cast<const float*>(shared ? p.ws_sh : p.ws) + (shared ? 0 : (int64_t)g * p.ws_stride);
@@ -223,8 +233,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
   // instruction, and read back at (run, mt, h, lane).  Row-major: rows in the swizzled
   // layout of the tokens.  (Packed rows past a ragged end of H are the layout's
   // padding: read, never stored.)
-  const uint8_t* wsrc[kWLd];
-  const int64_t wstep = t_packed ? 8192 : 128;
+  src.wstep = t_packed ? 8192 : 128;
 #pragma unroll
   for (int i = 0; i < kWLd; ++i) {
     const int q = (wave * kWLd + i) * 64 + lane;
@@ -232,14 +241,14 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     const int c = (q & 7) ^ ((r >> 1) & 7);
     if (t_packed) {
       const int bi = wave * kWLd + i;  // 1 KB block bi of the slab: block bi % 8 of run bi / 8
-      wsrc[i] = W + pack_w_offset(MOE_FP8_E4M3, K, nb, bi >> 3, 0) + (bi & 7) * 1024 + lane * 16;
+      src.w[i] = W + pack_w_offset(MOE_FP8_E4M3, K, nb, bi >> 3, 0) + (bi & 7) * 1024 + lane * 16;
     } else {
       int wrow;
       if (GEMM1)
         wrow = (r < 128 ? 0 : inter) + nb * 128 + (r & 127);
       else
         wrow = min(nb * BN + r, d.H - 1);
-      wsrc[i] = W + (int64_t)wrow * K + c * 16;
+      src.w[i] = W + (int64_t)wrow * K + c * 16;
     }
   }
   // scales, one 4-byte DMA per wave per slab (so every wave issues the same number of
@@ -248,28 +257,44 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
   // into sdummy
   const float* ws0 = WS + (int64_t)(GEMM1 ? nb : min(2 * nb, (d.H >> 7) - 1)) * KB;
   const float* ws1 = WS + (int64_t)(GEMM1 ? (inter >> 7) + nb : min(2 * nb + 1, (d.H >> 7) - 1)) * KB;
-  const float* ssrc;
   if (wave < kSxWaves) {
     const int m = min(m0 + 64 * wave + lane, M - 1);
     if (GEMM1 && shared) {
       const int s = m / d.T_s, tt = m - s * d.T_s;
-      ssrc = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
+      src.s = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
     } else {
-      const int wr = shared ? d.R + m : seg_row(T, d.S, m);
-      ssrc = p.as + (int64_t)wr * ((GEMM1 ? d.H : d.hstride) >> 7);
+      const int wr = shared ? d.R + m : seg_row(sg, d.S, m);
+      src.s = p.as + (int64_t)wr * ((GEMM1 ? d.H : d.hstride) >> 7);
     }
   } else {
-    ssrc = lane == 1 ? ws1 : ws0;
+    src.s = lane == 1 ? ws1 : ws0;
   }
+  return src;
+}
 
-  auto issue = [&](int kb, int st) {
+// The DMAs of K slab kb into ring stage st (every wave issues kLoadsPerSlab of them).
+__device__ __forceinline__ void issue_slab(const TileSrc& src, int kb, int st, Tiles& T) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kALd; ++i) dma16(asrc[i] + (int64_t)kb * 128, &T.a[st][(wave * kALd + i) * 1024]);
+  for (int i = 0; i < kALd; ++i) dma16(src.a[i] + (int64_t)kb * 128, &T.a[st][(wave * kALd + i) * 1024]);
 #pragma unroll
-    for (int i = 0; i < kWLd; ++i) dma16(wsrc[i] + (int64_t)kb * wstep, &T.w[st][(wave * kWLd + i) * 1024]);
-    float* sdst = wave < kSxWaves ? &T.sx[st][64 * wave] : (wave == kSxWaves ? &T.sw[st][0] : &T.sdummy[0]);
-    dma4(ssrc + kb, sdst);
-  };
+  for (int i = 0; i < kWLd; ++i) dma16(src.w[i] + (int64_t)kb * src.wstep, &T.w[st][(wave * kWLd + i) * 1024]);
+  float* sdst = wave < kSxWaves ? &T.sx[st][64 * wave] : (wave == kSxWaves ? &T.sw[st][0] : &T.sdummy[0]);
+  dma4(src.s + kb, sdst);
+}
+
+template <bool GEMM1, bool M32>
+__device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles& T, bool t_packed) {
+  const BatchDims& d = p.d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;  // token half, weight quarter
+  const bool shared = g == d.E;
+  const int inter = shared ? d.Ish : d.I;
+  const int K = GEMM1 ? d.H : inter;
+  const int KB = K >> 7;
+  const TileSrc src = make_src<GEMM1>(p, g, M, m0, nb, T.seg[0], t_packed);
+  auto issue = [&](int kb, int st) { issue_slab(src, kb, st, T); };
 
   const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
   constexpr int D = kStages - 1;  // slabs in flight ahead of the one multiplied
@@ -371,7 +396,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
         const int tr = wm * (BM / 2) + 32 * tt + r32;
         const int m = m0 + tr;
         if (m >= M) continue;
-        const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+        const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
         const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
@@ -389,7 +414,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       for (int tt = 0; tt < 4; ++tt) {
         const int m = m0 + wm * (BM / 2) + 32 * tt + r32;
         if (m >= M) continue;
-        const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+        const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -493,7 +518,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       const int tr = wm * (BM / 2) + 16 * tt + r16;
       const int m = m0 + tr;
       if (m >= M) continue;
-      const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+      const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
       const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
@@ -511,7 +536,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
     for (int tt = 0; tt < kTT; ++tt) {
       const int m = m0 + wm * (BM / 2) + 16 * tt + r16;
       if (m >= M) continue;
-      const int orow = shared ? d.R + m : seg_row(T, d.S, m);
+      const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = nb * BN + wrows[j] + 4 * g4;
@@ -559,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
     const int tm = (j / ncb) * kSTM + slot / kSTN, nb = (j % ncb) * kSTN + slot % kSTN;
     const int M = t.plan[kPlanRows + g];
     if (tm * BM >= M || nb >= nbg) continue;  // an empty slot (uniform)
-    segments(p, g, T);
+    segments(p, g, T.seg[0]);
     __syncthreads();
     tile_item<GEMM1, M32>(p, g, M, tm * BM, nb, T, t.packed != 0);
     __syncthreads();
