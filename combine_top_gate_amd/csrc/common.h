@@ -57,12 +57,13 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)v;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+typedef float cvt_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 cvt_b2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((cvt_f2){lo, hi}, cvt_b2));
 }
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return pack2_bf16(f, 0.f) & 0xFFFFu; }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

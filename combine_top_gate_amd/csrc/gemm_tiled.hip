@@ -57,8 +57,8 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kStride + ((c ^ ((
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(const LDS_AS uint8_t*)p; }
 
-// Memory -> LDS without registers: lane l of the wave writes its 16 (4) bytes at
-// dst + 16 l (4 l), dst wave-uniform; counted by vmcnt like any load.  Issued from
+// Memory -> LDS without registers: lane l of the wave writes its 16 (4) bytes at LDS
+// address dst + 16 l (4 l), dst wave-uniform; counted by vmcnt like any load.  Issued from
 // assembly: the compiler cannot tell which LDS stage such a load fills, and if it knew
 // of them it would wait for every one in flight (later stages included) before any
 // LDS read.  It does not need to know: the data is read only after wait7_barrier() /
@@ -66,8 +66,8 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(u
 // No register is written, so nothing of the load is left to land in a register.  M0
 // (the LDS base, read when the load issues) is saved and restored around it, with the
 // wait state an LDS-DMA needs after an M0 write.
-__device__ __forceinline__ void dma16(const void* src, const void* dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_off(dst));
+__device__ __forceinline__ void dma16(const void* src, uint32_t dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(dst);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
@@ -75,13 +75,25 @@ __device__ __forceinline__ void dma16(const void* src, const void* dst) {
       : "v"(src), "s"(base)
       : "memory");
 }
-__device__ __forceinline__ void dma4(const void* src, const void* dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_off(dst));
+__device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(dst);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(base)
+      : "memory");
+}
+// The same from a wave-uniform base (scalar registers) plus this lane's 32-bit offset:
+// lane l reads base + voff(l).  (No instruction offset: an LDS-DMA adds it to the LDS
+// address as well.)
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(m)
       : "memory");
 }
 // Wait until at most N of this wave's memory loads are in flight, then the workgroup
@@ -111,7 +123,12 @@ struct __align__(16) Tiles {
   float sw[kStages][64];    // weight scales of the staged slab (two 128-row blocks) in [0..1]
   float sdummy[64];         // where the idle lanes' scale loads go
   float amax[4][BM];        // GEMM1: per weight quarter, per token row
-  Segs seg[2];              // expert row segments of the current and the next item
+  Segs seg;                 // expert row segments of the item being set up
+  int rows[2][BM];          // row table of the current and the next item (row_table)
+  SrcPtrs src;              // GEMM1: the source buffers (the shared expert's rows), copied
+                            // once, so that a row's buffer is an LDS read, not a load
+  int pstart[MOE_MAX_EXPERTS + 2];  // this GEMM's plan: first super-tile of each group,
+  int prows[MOE_MAX_EXPERTS + 1];   // and its rows (copied once from the plan buffer)
   int item;
 };
 
@@ -125,6 +142,8 @@ constexpr int kXcds = 8;
 // g] rows of g; from [2 + 780] the 8 GEMM1 and 8 GEMM2 queue counters (zeroed here for
 // the launches that follow).
 constexpr int kPlanG1 = 2, kPlanG2 = 2 + 260, kPlanRows = 2 + 520, kPlanCtr = 2 + 780;
+// then 1 KB where epilogue lanes without an output store (see kEpiStores)
+constexpr int kPlanTrash = (kPlanCtr + 2 * kXcds + 15) / 16 * 16, kTrashWords = 256;
 
 __global__ __launch_bounds__(256) void k_plan(TiledArgs t) {
   const BatchDims& d = t.g1.d;
@@ -182,44 +201,65 @@ __device__ __forceinline__ int seg_row(const Segs& T, int S, int m) {
   return T.row0[s] + (m - T.pre[s]);
 }
 
+// The rows of token tile [m0, m0 + BM) of group g (M rows), one per tile row, built once
+// per item by the workgroup (then an LDS read wherever a row is needed): the window row
+// (GEMM2: the h row; the shared expert's are R + m), or for GEMM1's shared expert the
+// token index m.  Rows past M repeat the last one (their loads are harmless, their
+// results never stored).  Ends with a barrier.
+template <bool GEMM1>
+__device__ __forceinline__ void row_table(const GemmArgs& p, int g, int M, int m0, const Segs& sg, int* rows) {
+  const BatchDims& d = p.d;
+  for (int r = threadIdx.x; r < BM; r += kThreads) {
+    const int m = min(m0 + r, M - 1);
+    rows[r] = g == d.E ? (GEMM1 ? m : d.R + m) : seg_row(sg, d.S, m);
+  }
+  __syncthreads();
+}
+
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// One item: token tile [m0, m0 + BM) of group g (M rows), weight block nb.  M32: the K
-// loop on v_mfma_scale_f32_32x32x64_f8f6f4 instead of 16x16x128 (see below).
 // This thread's DMA sources for one work item (token tile [m0, m0 + BM) of group g with M
 // rows, weight block nb).  Instruction i of wave w fills the 1 KB at 16 * ((w * n + i) * 64
 // + lane) of a stage buffer: chunk p = (w * n + i) * 64 + lane is physical chunk p % 8 of
 // row p / 8, which holds that row's logical chunk (p % 8) ^ ((row >> 1) & 7) (the swizzle
 // of swz()).
+// PK (packed weights): every DMA of a wave's weight pieces reads one run at consecutive
+// 1 KB blocks, so one wave-uniform base (scalar registers) replaces per-lane pointers.
+static_assert(8 % kWLd == 0, "a wave's weight pieces lie in one packed run");
+template <bool PK>
 struct TileSrc {
   const uint8_t* a[kALd];
-  const uint8_t* w[kWLd];
+  const uint8_t* w[PK ? 1 : kWLd];
   const float* s;
-  int64_t wstep;
 };
 
-template <bool GEMM1>
-__device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int m0, int nb, const Segs& sg,
-                                            bool t_packed) {
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <bool GEMM1, bool PK>
+__device__ __forceinline__ TileSrc<PK> make_src(const GemmArgs& p, int g, int nb, const int* rows, const Tiles& T) {
   const BatchDims& d = p.d;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
   const int K = GEMM1 ? d.H : inter;
   const int KB = K >> 7;
-  TileSrc src;
+  TileSrc<PK> src;
 #pragma unroll
   for (int i = 0; i < kALd; ++i) {
     const int q = (wave * kALd + i) * 64 + lane;
     const int r = q >> 3;
     const int c = (q & 7) ^ ((r >> 1) & 7);
-    const int m = min(m0 + r, M - 1);   // rows past the end repeat the last one (not stored)
+    const int wr = rows[r];
     const uint8_t* rowp;
     if (GEMM1 && shared) {
-      const int s = m / d.T_s, tt = m - s * d.T_s;
-      rowp = p.src.x[s] + (int64_t)tt * d.H;
+      const int s = wr / d.T_s, tt = wr - s * d.T_s;  // token index -> its source buffer
+      rowp = T.src.x[s] + (int64_t)tt * d.H;
     } else {
-      const int wr = shared ? d.R + m : seg_row(sg, d.S, m);
       rowp = p.a + (int64_t)wr * (GEMM1 ? d.H : d.hstride);
     }
     src.a[i] = rowp + c * 16;
@@ -233,16 +273,16 @@ __device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int
   // instruction, and read back at (run, mt, h, lane).  Row-major: rows in the swizzled
   // layout of the tokens.  (Packed rows past a ragged end of H are the layout's
   // padding: read, never stored.)
-  src.wstep = t_packed ? 8192 : 128;
+  if constexpr (PK) {
+    const int bi = wave * kWLd;  // 1 KB block bi of the slab: block bi % 8 of run bi / 8
+    src.w[0] = uniform_ptr(W + pack_w_offset(MOE_FP8_E4M3, K, nb, bi >> 3, 0) + (bi & 7) * 1024);
+  } else {
 #pragma unroll
   for (int i = 0; i < kWLd; ++i) {
     const int q = (wave * kWLd + i) * 64 + lane;
     const int r = q >> 3;  // 0..255
     const int c = (q & 7) ^ ((r >> 1) & 7);
-    if (t_packed) {
-      const int bi = wave * kWLd + i;  // 1 KB block bi of the slab: block bi % 8 of run bi / 8
-      src.w[i] = W + pack_w_offset(MOE_FP8_E4M3, K, nb, bi >> 3, 0) + (bi & 7) * 1024 + lane * 16;
-    } else {
+    {
       int wrow;
       if (GEMM1)
         wrow = (r < 128 ? 0 : inter) + nb * 128 + (r & 127);
@@ -251,6 +291,7 @@ __device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int
       src.w[i] = W + (int64_t)wrow * K + c * 16;
     }
   }
+  }
   // scales, one 4-byte DMA per wave per slab (so every wave issues the same number of
   // loads per slab): waves w < kSxWaves the token scales of rows 64 w + lane, wave
   // kSxWaves in lanes 0-1 the weight scales of the tile's two 128-row blocks, the rest
@@ -258,12 +299,11 @@ __device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int
   const float* ws0 = WS + (int64_t)(GEMM1 ? nb : min(2 * nb, (d.H >> 7) - 1)) * KB;
   const float* ws1 = WS + (int64_t)(GEMM1 ? (inter >> 7) + nb : min(2 * nb + 1, (d.H >> 7) - 1)) * KB;
   if (wave < kSxWaves) {
-    const int m = min(m0 + 64 * wave + lane, M - 1);
+    const int wr = rows[64 * wave + lane];
     if (GEMM1 && shared) {
-      const int s = m / d.T_s, tt = m - s * d.T_s;
-      src.s = p.src.xs[s] + (int64_t)tt * (d.H >> 7);
+      const int s = wr / d.T_s, tt = wr - s * d.T_s;
+      src.s = T.src.xs[s] + (int64_t)tt * (d.H >> 7);
     } else {
-      const int wr = shared ? d.R + m : seg_row(sg, d.S, m);
       src.s = p.as + (int64_t)wr * ((GEMM1 ? d.H : d.hstride) >> 7);
     }
   } else {
@@ -273,32 +313,50 @@ __device__ __forceinline__ TileSrc make_src(const GemmArgs& p, int g, int M, int
 }
 
 // The DMAs of K slab kb into ring stage st (every wave issues kLoadsPerSlab of them).
-__device__ __forceinline__ void issue_slab(const TileSrc& src, int kb, int st, Tiles& T) {
-  const int wave = threadIdx.x >> 6;
+template <bool PK>
+__device__ __forceinline__ void issue_slab(const TileSrc<PK>& src, int kb, int st, Tiles& T) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // LDS addresses as plain offsets from the tile buffers' base (uniform, scalar registers)
+  const uint32_t t0 = __builtin_amdgcn_readfirstlane(lds_off(&T));
 #pragma unroll
-  for (int i = 0; i < kALd; ++i) dma16(src.a[i] + (int64_t)kb * 128, &T.a[st][(wave * kALd + i) * 1024]);
+  for (int i = 0; i < kALd; ++i)
+    dma16(src.a[i] + (int64_t)kb * 128, t0 + offsetof(Tiles, a) + st * (BM * kStride) + (wave * kALd + i) * 1024);
+  const uint32_t wdst = t0 + offsetof(Tiles, w) + st * (BN * kStride) + wave * kWLd * 1024;
+  if constexpr (PK) {
+    const uint8_t* wb = src.w[0] + (int64_t)kb * 8192;  // uniform
+    static_assert(kWLd == 4, "four 1 KB weight pieces per wave and slab");
 #pragma unroll
-  for (int i = 0; i < kWLd; ++i) dma16(src.w[i] + (int64_t)kb * src.wstep, &T.w[st][(wave * kWLd + i) * 1024]);
-  float* sdst = wave < kSxWaves ? &T.sx[st][64 * wave] : (wave == kSxWaves ? &T.sw[st][0] : &T.sdummy[0]);
+    for (int i = 0; i < kWLd; ++i) dma16s(wb, i * 1024 + lane * 16, wdst + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kWLd; ++i) dma16(src.w[i] + (int64_t)kb * 128, wdst + i * 1024);
+  }
+  const uint32_t sdst = wave < kSxWaves ? t0 + offsetof(Tiles, sx) + (st * BM + 64 * wave) * 4
+                        : wave == kSxWaves ? t0 + offsetof(Tiles, sw) + st * 64 * 4
+                                           : t0 + offsetof(Tiles, sdummy);
   dma4(src.s + kb, sdst);
 }
 
-template <bool GEMM1, bool M32>
-__device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles& T, bool t_packed) {
+// One item on 32x32x64 MFMAs (option): token tile [m0, m0 + BM) of group g (M rows),
+// weight block nb, segments in T.seg; loads, K loop and epilogue in sequence.
+template <bool GEMM1, bool PK>
+__device__ void tile_item_m32(const GemmArgs& p, int g, int M, int m0, int nb, Tiles& T) {
+  constexpr bool t_packed = PK;
   const BatchDims& d = p.d;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
   const int wm = wave >> 2, wn = wave & 3;  // token half, weight quarter
   const bool shared = g == d.E;
   const int inter = shared ? d.Ish : d.I;
   const int K = GEMM1 ? d.H : inter;
   const int KB = K >> 7;
-  const TileSrc src = make_src<GEMM1>(p, g, M, m0, nb, T.seg[0], t_packed);
-  auto issue = [&](int kb, int st) { issue_slab(src, kb, st, T); };
+  row_table<GEMM1>(p, g, M, m0, T.seg, T.rows[0]);
+  const TileSrc<PK> src = make_src<GEMM1, PK>(p, g, nb, T.rows[0], T);
+  auto issue = [&](int kb, int st) { issue_slab<PK>(src, kb, st, T); };
 
   const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
   constexpr int D = kStages - 1;  // slabs in flight ahead of the one multiplied
-  if constexpr (M32) {
+  {
     // 32x32x64 MFMAs.  This wave's 64 weight rows are 2 tiles of 32 (GEMM1: gate rows
     // wn*32 + r and up rows 128 + wn*32 + r; GEMM2: rows wn*64 + 32 j + r) and its 128
     // token rows 4 tiles of 32 (wm*128 + 32 tt + r).  Operand lane l holds row (column)
@@ -396,7 +454,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
         const int tr = wm * (BM / 2) + 32 * tt + r32;
         const int m = m0 + tr;
         if (m >= M) continue;
-        const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
+        const int orow = GEMM1 && shared ? d.R + T.rows[0][m - m0] : T.rows[0][m - m0];
         const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
@@ -414,7 +472,7 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       for (int tt = 0; tt < 4; ++tt) {
         const int m = m0 + wm * (BM / 2) + 32 * tt + r32;
         if (m >= M) continue;
-        const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
+        const int orow = GEMM1 && shared ? d.R + T.rows[0][m - m0] : T.rows[0][m - m0];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -427,57 +485,159 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
           }
       }
     }
-    return;
-  } else {
-  // this wave: token tiles wm*(BM/2) + 16*tt (tt < kTT); weight tiles (GEMM1) gate rows
-  // wn*32 + 16*j and up rows 128 + wn*32 + 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j
-  int wrows[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    wrows[j] = GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
-  // byte offsets (within a stage) of this lane's fragments
+  }
+}
+
+
+// ---- the default K loop (16x16x128), with work items pipelined.  When an item's K loop
+// ends, the ring is idle: the next item's first two slabs are issued into it before this
+// item's epilogue runs, so their latency overlaps the epilogue, and the epilogue's stores
+// drain while the next K loop runs.  Vector-memory stores count in the same in-order
+// counter (vmcnt) as the slab loads, so the next K loop must know how many stores follow
+// its first slabs: every lane of every wave stores in each of the epilogue's store
+// instructions (a lane without an output writes to a scratch area of the plan buffer),
+// and they are issued from assembly, so that the compiler neither skips nor merges any.
+template <bool GEMM1>
+constexpr int kEpiStores = GEMM1 ? 3 * kTT : 4 * kTT;  // GEMM1: h (2 per token tile) + scale
+
+template <int OFF = 0>
+__device__ __forceinline__ void store32(void* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off offset:%2" ::"v"(p), "v"(v), "n"(OFF) : "memory");
+}
+template <int OFF = 0>
+__device__ __forceinline__ void store64(void* p, uint64_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off offset:%2" ::"v"(p), "v"(v), "n"(OFF) : "memory");
+}
+// LDS-only workgroup barrier (leaves the memory loads and stores in flight)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct Item {
+  int g, M, m0, nb;
+};
+
+// The next work item from the per-XCD queues (see k_tiled), or false when every queue is
+// exhausted.  Uniform over the workgroup; uses T.item and two barriers per queue entry.
+template <bool GEMM1>
+__device__ bool next_item(const TiledArgs& t, Tiles& T, int& q, int& left, Item& it) {
+  const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
+  const BatchDims& d = p.d;
+  const int nG = d.E + (d.Ish ? 1 : 0);
+  const int n_sup = t.plan[GEMM1 ? 0 : 1];
+  int* ctr = t.plan + kPlanCtr + (GEMM1 ? 0 : kXcds);
+  while (left > 0) {
+    if (threadIdx.x == 0) T.item = atomicAdd(ctr + q, 1);
+    __syncthreads();
+    const int k = __builtin_amdgcn_readfirstlane(T.item);
+    __syncthreads();  // T.item is rewritten by the next round
+    const int sup = q + kXcds * (k / kSlots), slot = k % kSlots;
+    if (sup >= n_sup) {  // this queue is exhausted (uniform): move on to the next
+      q = (q + 1) % kXcds;
+      --left;
+      continue;
+    }
+    // the group of super-tile sup: the last g with pstart[g] <= sup (groups without
+    // super-tiles share their successor's start)
+    int lo = 0, hi = nG - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (T.pstart[mid] <= sup) lo = mid; else hi = mid - 1;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int nbg = GEMM1 ? (g < d.E ? t.nb1_r : t.nb1_s) : t.nb2;
+    const int ncb = (nbg + kSTN - 1) / kSTN;  // column super-blocks of g
+    const int j = sup - T.pstart[g];
+    const int tm = (j / ncb) * kSTM + slot / kSTN, nb = (j % ncb) * kSTN + slot % kSTN;
+    const int M = __builtin_amdgcn_readfirstlane(T.prows[g]);
+    if (tm * BM >= M || nb >= nbg) continue;  // an empty slot (uniform)
+    // uniform values, held in scalar registers (the K loop needs every vector register)
+    it = Item{g, M, __builtin_amdgcn_readfirstlane(tm * BM), __builtin_amdgcn_readfirstlane(nb)};
+    return true;
+  }
+  return false;
+}
+
+// This GEMM's plan into LDS (read by next_item after its first barrier).
+template <bool GEMM1>
+__device__ __forceinline__ void load_plan(const TiledArgs& t, Tiles& T) {
+  const BatchDims& d = (GEMM1 ? t.g1 : t.g2).d;
+  const int nG = d.E + (d.Ish ? 1 : 0);
+  const int* start = t.plan + (GEMM1 ? kPlanG1 : kPlanG2);
+  for (int g = threadIdx.x; g <= nG; g += kThreads) {
+    T.pstart[g] = start[g];
+    if (g < nG) T.prows[g] = t.plan[kPlanRows + g];
+  }
+}
+
+template <bool GEMM1>
+__device__ __forceinline__ int item_kb(const GemmArgs& p, int g) {
+  return (GEMM1 ? p.d.H : (g == p.d.E ? p.d.Ish : p.d.I)) >> 7;
+}
+
+// Issues an item's slab 0 into stage 0 and (when it has more) slab 1 into stage 1; the
+// ring must be idle.
+template <bool GEMM1, bool PK>
+__device__ __forceinline__ void issue_first(const GemmArgs& p, const Item& it, const int* rows, Tiles& T) {
+  const TileSrc<PK> src = make_src<GEMM1, PK>(p, it.g, it.nb, rows, T);
+  issue_slab<PK>(src, 0, 0, T);
+  if (item_kb<GEMM1>(p, it.g) > 1) issue_slab<PK>(src, 1, 1, T);
+}
+
+// This wave's weight tiles: (GEMM1) gate rows wn*32 + 16*j and up rows 128 + wn*32 +
+// 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j.  Its token tiles: wm*(BM/2) + 16*tt.
+template <bool GEMM1>
+__device__ __forceinline__ int wave_row(int wn, int j) {
+  return GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
+}
+
+// acc[j][tt] = sum over K slabs of the MFMA result times (weight scale x token scale).
+// On entry slab 0 (stage 0) and, if KB > 1, slab 1 (stage 1) are in flight, followed by
+// exactly kEpiStores<GEMM1> stores of this wave (the previous item's epilogue, or
+// placeholders before the first item).  From step 1 on, step kb issues slab kb + 1 into
+// the stage read at step kb - 1.  Steps 0 and 1 are written out, so that every wait
+// count is a constant and the loop itself is one uniform body.
+template <bool GEMM1, bool PK>
+__device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& src, Tiles& T, int KB) {
+  constexpr bool t_packed = PK;
+  constexpr int S = kEpiStores<GEMM1>;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int wsel = GEMM1 ? -1 : (wn >> 1);  // GEMM2: this wave's 64 rows lie in block wn/2
   // Fragment offsets: tiles lie 16 or 128 rows apart, which leaves the swizzle term
   // (r >> 1) & 7 unchanged, so every fragment is a base (two registers per operand)
   // plus a constant the LDS instructions take as an immediate.
-  const int w0 = t_packed ? wn * 8192 + lane * 16 : swz(wrows[0] + r16, g4);
-  const int w1 = t_packed ? w0 + 1024 : swz(wrows[0] + r16, g4 + 4);
+  const int r0 = wave_row<GEMM1>(wn, 0);
+  const int w0 = t_packed ? wn * 8192 + lane * 16 : swz(r0 + r16, g4);
+  const int w1 = t_packed ? w0 + 1024 : swz(r0 + r16, g4 + 4);
   const int a0 = swz(wm * (BM / 2) + r16, g4), a1 = swz(wm * (BM / 2) + r16, g4 + 4);
   auto wfrag_off = [&](int j, int h) {  // weight tile j, half h
     const int base = h ? w1 : w0;
-    return t_packed ? base + 2 * j * 1024 : base + (wrows[j] - wrows[0]) * kStride;
+    return t_packed ? base + 2 * j * 1024 : base + (wave_row<GEMM1>(wn, j) - r0) * kStride;
   };
-
-  v4f acc[4][kTT];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // the previous item's last reads of the ring are done
-#pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (i < KB) issue(i, i);
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb % kStages;
-    // this wave's loads of slab kb have landed (those of the D - 1 later slabs may stay
-    // in flight), then every wave's; stage (kb + D) % kStages was last read at kb - 1
-    if (D > 1 && kb + D - 1 < KB)
-      wait_barrier<(D > 1 ? D - 1 : 0) * kLoadsPerSlab>();
-    else
-      wait_barrier<0>();
-    if (kb + D < KB) issue(kb + D, (kb + D) % kStages);
-    const uint8_t* ws_ = T.w[st];
-    const uint8_t* as_ = T.a[st];
+  // LDS reads through an LDS-space pointer: per-lane offsets plus constants the LDS
+  // instructions take as immediates
+  const LDS_AS uint8_t* L = (const LDS_AS uint8_t*)(const uint8_t*)(&T);
+  const int sxo = (wm * (BM / 2) + r16) * 4;
+  auto compute = [&](int st) {
+    const LDS_AS uint8_t* ws_ = L + offsetof(Tiles, w) + st * (BN * kStride);
+    const LDS_AS uint8_t* as_ = L + offsetof(Tiles, a) + st * (BM * kStride);
+    const LDS_AS uint8_t* sx_ = L + offsetof(Tiles, sx) + st * (BM * 4) + sxo;
+    const LDS_AS float* sw_ = reinterpret_cast<const LDS_AS float*>(L + offsetof(Tiles, sw) + st * 64 * 4);
     u32x4 wf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
-    const float swj[2] = {T.sw[st][0], T.sw[st][1]};
+    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const LDS_AS u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
+    const float swj[2] = {sw_[0], sw_[1]};
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(as_ + a0 + tt * 16 * kStride);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(as_ + a1 + tt * 16 * kStride);
+      const u32x4 x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + tt * 16 * kStride);
+      const u32x4 x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + tt * 16 * kStride);
       const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      const float sx = T.sx[st][wm * (BM / 2) + 16 * tt + r16];
+      const float sx = *reinterpret_cast<const LDS_AS float*>(sx_ + 64 * tt);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v8i wv = {(int)wf[2 * j].x, (int)wf[2 * j].y, (int)wf[2 * j].z, (int)wf[2 * j].w,
@@ -491,9 +651,46 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
         acc[j][tt][3] = fmaf(r[3], sc, acc[j][tt][3]);
       }
     }
+  };
+  // each wait: this wave's loads of the slab have landed (what was issued after it may
+  // stay in flight), then the barrier: every wave's have
+  if (KB > 1)
+    wait_barrier<kLoadsPerSlab + S>();
+  else
+    wait_barrier<S>();
+  compute(0);
+  if (KB == 1) return;
+  wait_barrier<S>();
+  if (KB > 2) issue_slab<PK>(src, 2, 0, T);
+  compute(1);
+  for (int kb = 2; kb < KB; ++kb) {
+    wait_barrier<0>();
+    if (kb + 1 < KB) issue_slab<PK>(src, kb + 1, (kb + 1) & 1, T);
+    compute(kb & 1);
   }
+}
 
-  // ---- epilogue; lane holds weight rows wrows[j] + 4*g4 + i of token wm*(BM/2) + 16*tt + r16
+// The kEpiStores<GEMM1> placeholder stores that stand in for an epilogue's before the
+// first item's K loop.
+template <bool GEMM1>
+__device__ __forceinline__ void placeholder_stores(int* plan) {
+  uint8_t* trash = reinterpret_cast<uint8_t*>(plan + kPlanTrash) + 8 * (threadIdx.x & 63);
+#pragma unroll
+  for (int i = 0; i < kEpiStores<GEMM1>; ++i) store32(trash, 0u);
+}
+
+// The epilogue of an item: exactly kEpiStores<GEMM1> store instructions per wave.  Lane
+// (g4, r16) holds weight rows wave_row(wn, j) + 4*g4 + i of token wm*(BM/2) + 16*tt + r16.
+template <bool GEMM1>
+__device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, const int* rows, v4f (&acc)[4][kTT],
+                                           Tiles& T, int* plan) {
+  const BatchDims& d = p.d;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  // lanes without an output store here (1 KB: lane offsets up to 504 plus store offsets)
+  uint8_t* trash = reinterpret_cast<uint8_t*>(plan + kPlanTrash) + 8 * lane;
+  const bool shared = it.g == d.E;
   if constexpr (GEMM1) {
     // SwiGLU in place: acc[j] (gate, j = 0, 1) becomes h; acc[2 + j] (up) is then dead
 #pragma unroll
@@ -511,42 +708,86 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       if (g4 == 0) T.amax[wn][wm * (BM / 2) + 16 * tt + r16] = mx;
     }
-    __syncthreads();
+    lds_barrier();
     const int hsc_stride = d.hstride >> 7;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
       const int tr = wm * (BM / 2) + 16 * tt + r16;
-      const int m = m0 + tr;
-      if (m >= M) continue;
-      const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
+      const bool ok = it.m0 + tr < it.M;
+      const int orow = shared ? d.R + rows[tr] : rows[tr];
       const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      uint32_t code[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float q[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[j][tt][i] / sc, -448.0f), 448.0f);
-        *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow * d.hstride + nb * 128 + wn * 32 + 16 * j + 4 * g4) =
-            pack4_e4m3(q[0], q[1], q[2], q[3]);
+        code[j] = pack4_e4m3(q[0], q[1], q[2], q[3]);
       }
-      if (wn == 0 && g4 == 0) p.hs[(int64_t)orow * hsc_stride + nb] = sc;
+      // this lane's h columns nb*128 + wn*32 + 16 j + 4 g4 .. + 3 (j = 0, 1: 16 bytes apart)
+      uint8_t* hp = ok ? p.h + (int64_t)orow * d.hstride + it.nb * 128 + wn * 32 + 4 * g4 : trash;
+      store32<0>(hp, code[0]);
+      store32<16>(hp, code[1]);
+      uint8_t* sp = ok && wn == 0 && g4 == 0 ? reinterpret_cast<uint8_t*>(p.hs + (int64_t)orow * hsc_stride + it.nb)
+                                             : trash;
+      store32<0>(sp, __float_as_uint(sc));
     }
   } else {
+    // this wave's 64 columns are all inside H or all past it (H is a multiple of 128)
+    const bool col_ok = it.nb * BN + wn * 64 < d.H;
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      const int m = m0 + wm * (BM / 2) + 16 * tt + r16;
-      if (m >= M) continue;
-      const int orow = shared ? d.R + m : seg_row(T.seg[0], d.S, m);
+      const int tr = wm * (BM / 2) + 16 * tt + r16;
+      const bool ok = col_ok && it.m0 + tr < it.M;
+      // columns nb*BN + wn*64 + 16 j + 4 g4 .. + 3 (j = 0..3: 32 bytes apart)
+      uint8_t* yp = ok ? reinterpret_cast<uint8_t*>(p.y + (int64_t)rows[tr] * d.H + it.nb * BN + wn * 64 + 4 * g4)
+                       : trash;
+      uint64_t v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = nb * BN + wrows[j] + 4 * g4;
-        if (n >= d.H) continue;
-        const uint32_t lo = bf16_bits(acc[j][tt][0]) | (bf16_bits(acc[j][tt][1]) << 16);
-        const uint32_t hi = bf16_bits(acc[j][tt][2]) | (bf16_bits(acc[j][tt][3]) << 16);
-        *reinterpret_cast<uint2*>(p.y + (int64_t)orow * d.H + n) = make_uint2(lo, hi);
-      }
+      for (int j = 0; j < 4; ++j)
+        v[j] = pack2_bf16(acc[j][tt][0], acc[j][tt][1]) | ((uint64_t)pack2_bf16(acc[j][tt][2], acc[j][tt][3]) << 32);
+      store64<0>(yp, v[0]);
+      store64<32>(yp, v[1]);
+      store64<64>(yp, v[2]);
+      store64<96>(yp, v[3]);
     }
   }
+}
+
+// The persistent loop of the default path: items from the queues; the next item's first
+// two slabs are issued before this item's epilogue.
+template <bool GEMM1, bool PK>
+__device__ void run16(const TiledArgs& t, Tiles& T) {
+  const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
+  int q = blockIdx.x % kXcds, left = kXcds;
+  Item it;
+  if (!next_item<GEMM1>(t, T, q, left, it)) return;
+  int sb = 0;  // T.rows[sb]: the current item's row table
+  segments(p, it.g, T.seg);
+  __syncthreads();
+  row_table<GEMM1>(p, it.g, it.M, it.m0, T.seg, T.rows[sb]);
+  issue_first<GEMM1, PK>(p, it, T.rows[sb], T);
+  placeholder_stores<GEMM1>(t.plan);
+  for (;;) {
+    v4f acc[4][kTT];
+    {
+      const TileSrc<PK> src = make_src<GEMM1, PK>(p, it.g, it.nb, T.rows[sb], T);
+      kloop16<GEMM1, PK>(acc, src, T, item_kb<GEMM1>(p, it.g));
+    }
+    Item nx;
+    // its barriers also end every wave's reads of the ring
+    const bool more = next_item<GEMM1>(t, T, q, left, nx);
+    if (more) {
+      segments(p, nx.g, T.seg);
+      __syncthreads();
+      row_table<GEMM1>(p, nx.g, nx.M, nx.m0, T.seg, T.rows[sb ^ 1]);
+      issue_first<GEMM1, PK>(p, nx, T.rows[sb ^ 1], T);
+    }
+    epilogue16<GEMM1>(p, it, T.rows[sb], acc, T, t.plan);
+    if (!more) break;
+    it = nx;
+    sb ^= 1;
   }
 }
 
@@ -555,40 +796,41 @@ __device__ void tile_item(const GemmArgs& p, int g, int M, int m0, int nb, Tiles
 // Workgroup b runs on XCD b % 8 (the GPU's round-robin placement; any other placement
 // only costs locality).  Slots past an expert's last token tile or column block are
 // empty.  A workgroup leaves when every queue is exhausted.
-template <bool GEMM1, bool M32>
+template <bool GEMM1, bool M32, bool PK>
 __global__ __launch_bounds__(kThreads, 1) void k_tiled(TiledArgs t) {
   __shared__ Tiles T;
-  const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
-  const BatchDims& d = p.d;
-  const int nG = d.E + (d.Ish ? 1 : 0);
-  const int* start = t.plan + (GEMM1 ? kPlanG1 : kPlanG2);
-  const int n_sup = t.plan[GEMM1 ? 0 : 1];
-  int* ctr = t.plan + kPlanCtr + (GEMM1 ? 0 : kXcds);
-  int q = blockIdx.x % kXcds;
-  for (int left = kXcds; left > 0;) {
-    if (threadIdx.x == 0) T.item = atomicAdd(ctr + q, 1);
-    __syncthreads();
-    const int k = T.item;
-    __syncthreads();  // T.item is rewritten by the next round
-    const int sup = q + kXcds * (k / kSlots), slot = k % kSlots;
-    if (sup >= n_sup) {  // this queue is exhausted (uniform): move on to the next
-      q = (q + 1) % kXcds;
-      --left;
-      continue;
-    }
-    int g = 0;
-    while (g + 1 < nG && sup >= start[g + 1]) ++g;
-    const int nbg = GEMM1 ? (g < d.E ? t.nb1_r : t.nb1_s) : t.nb2;
-    const int ncb = (nbg + kSTN - 1) / kSTN;  // column super-blocks of g
-    const int j = sup - start[g];
-    const int tm = (j / ncb) * kSTM + slot / kSTN, nb = (j % ncb) * kSTN + slot % kSTN;
-    const int M = t.plan[kPlanRows + g];
-    if (tm * BM >= M || nb >= nbg) continue;  // an empty slot (uniform)
-    segments(p, g, T.seg[0]);
-    __syncthreads();
-    tile_item<GEMM1, M32>(p, g, M, tm * BM, nb, T, t.packed != 0);
-    __syncthreads();
+  if (GEMM1 && threadIdx.x < MOE_MAX_SRC) {
+    T.src.x[threadIdx.x] = t.g1.src.x[threadIdx.x];
+    T.src.xs[threadIdx.x] = t.g1.src.xs[threadIdx.x];
   }
+  load_plan<GEMM1>(t, T);  // both published by next_item's first barrier
+  if constexpr (!M32) {
+    run16<GEMM1, PK>(t, T);
+  } else {
+    const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
+    int q = blockIdx.x % kXcds, left = kXcds;
+    Item it;
+    while (next_item<GEMM1>(t, T, q, left, it)) {
+      segments(p, it.g, T.seg);
+      __syncthreads();
+      tile_item_m32<GEMM1, PK>(p, it.g, it.M, it.m0, it.nb, T);
+      __syncthreads();
+    }
+  }
+}
+
+template <bool GEMM1>
+hipError_t launch_one(const TiledArgs& a, int grid, hipStream_t st) {
+  const dim3 g(grid), b(kThreads);
+  if (a.m32 && a.packed)
+    hipLaunchKernelGGL((k_tiled<GEMM1, true, true>), g, b, 0, st, a);
+  else if (a.m32)
+    hipLaunchKernelGGL((k_tiled<GEMM1, true, false>), g, b, 0, st, a);
+  else if (a.packed)
+    hipLaunchKernelGGL((k_tiled<GEMM1, false, true>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_tiled<GEMM1, false, false>), g, b, 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -597,16 +839,8 @@ hipError_t launch_tiled(const TiledArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.m32)
-    hipLaunchKernelGGL((k_tiled<true, true>), dim3(grid), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_tiled<true, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.m32)
-    hipLaunchKernelGGL((k_tiled<false, true>), dim3(grid), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_tiled<false, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  if ((e = launch_one<true>(a, grid, st)) != hipSuccess) return e;
+  return launch_one<false>(a, grid, st);
 }
 
-int tiled_plan_words() { return kPlanCtr + 2 * kXcds; }
+int tiled_plan_words() { return kPlanTrash + kTrashWords; }

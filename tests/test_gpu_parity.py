@@ -135,6 +135,11 @@ def test_gemm_schedules_give_identical_output(name, over):
     ("prefill4096_zipf_fp8", dict(S=4, T_s=96, H=512, I=256, E=8, k=4, seed=61), True),
     ("prefill4096_zipf_fp8", dict(S=3, T_s=80, H=384, I=384, E=5, k=3, seed=62), True),
     ("decode128_fp8", dict(S=3, T_s=7, H=384, I=256, E=5, k=3, seed=63), True),
+    # one K slab in GEMM1 and GEMM2 (H = I = 128), one in GEMM2 only, and the shared
+    # expert (FP8) through the tiled kernels
+    ("prefill4096_zipf_fp8", dict(S=2, T_s=80, H=128, I=128, E=4, k=2, seed=64), True),
+    ("prefill4096_zipf_fp8", dict(S=2, T_s=80, H=256, I=128, E=4, k=2, seed=65), False),
+    ("decode128_fp8", dict(S=3, T_s=40, H=256, I=256, E=4, k=2, shared_I=384, seed=66), True),
 ])
 def test_tiled_gemm_matches_oracle_and_streaming_kernel(name, over, packed):
     """The LDS-tiled kernels (large experts) against the oracle, and bit for bit against
