@@ -67,4 +67,9 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) { return pack2_bf16(f, 0.
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU with the hardware reciprocal (v_rcp_f32, 1 ulp) in place of an IEEE division.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// A value of a 1x128 block divided by the block's fp32 scale, clamped to the e4m3 range:
+// inv_sc = __builtin_amdgcn_rcpf(scale), computed once per block (v_rcp_f32, 1 ulp).
+__device__ __forceinline__ float e4m3_scaled(float v, float inv_sc) { return fminf(fmaxf(v * inv_sc, -448.0f), 448.0f); }

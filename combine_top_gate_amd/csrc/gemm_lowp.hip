@@ -553,11 +553,12 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
     const int tk = nt * 16 + r16;
     const float amax = fmaxf(fmaxf(s_amax[0][tk], s_amax[1][tk]), fmaxf(s_amax[2][tk], s_amax[3][tk]));
     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float inv = __builtin_amdgcn_rcpf(sc);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float q[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(hv[t][nt][i] / sc, -448.0f), 448.0f);
+      for (int i = 0; i < 4; ++i) q[i] = e4m3_scaled(hv[t][nt][i], inv);
       *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow[nt] * d.hstride + rb + 16 * t + 4 * g4) =
           pack4_e4m3(q[0], q[1], q[2], q[3]);
     }

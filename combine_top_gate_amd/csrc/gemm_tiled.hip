@@ -457,11 +457,12 @@ __device__ void tile_item_m32(const GemmArgs& p, int g, int M, int m0, int nb, T
         const int orow = GEMM1 && shared ? d.R + T.rows[0][m - m0] : T.rows[0][m - m0];
         const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        const float inv = __builtin_amdgcn_rcpf(sc);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           float q[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[0][tt][4 * i4 + i] / sc, -448.0f), 448.0f);
+          for (int i = 0; i < 4; ++i) q[i] = e4m3_scaled(acc[0][tt][4 * i4 + i], inv);
           *reinterpret_cast<uint32_t*>(p.h + (int64_t)orow * d.hstride + nb * 128 + wn * 32 + 8 * i4 + 4 * g2) =
               pack4_e4m3(q[0], q[1], q[2], q[3]);
         }
@@ -717,12 +718,13 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, co
       const int orow = shared ? d.R + rows[tr] : rows[tr];
       const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      const float inv = __builtin_amdgcn_rcpf(sc);
       uint32_t code[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float q[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[j][tt][i] / sc, -448.0f), 448.0f);
+        for (int i = 0; i < 4; ++i) q[i] = e4m3_scaled(acc[j][tt][i], inv);
         code[j] = pack4_e4m3(q[0], q[1], q[2], q[3]);
       }
       // this lane's h columns nb*128 + wn*32 + 16 j + 4 g4 .. + 3 (j = 0, 1: 16 bytes apart)
