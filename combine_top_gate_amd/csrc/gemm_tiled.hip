@@ -633,12 +633,22 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
 #pragma unroll
     for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const LDS_AS u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
     const float swj[2] = {sw_[0], sw_[1]};
+    // GEMM1: token fragments one tile ahead, the LDS reads of tile tt + 1 in flight while
+    // the MFMAs of tile tt run (GEMM2 has no registers to spare for them)
+    u32x4 x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0);
+    u32x4 x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1);
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      const u32x4 x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + tt * 16 * kStride);
-      const u32x4 x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + tt * 16 * kStride);
+      if (!GEMM1 && tt > 0) {
+        x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + tt * 16 * kStride);
+        x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + tt * 16 * kStride);
+      }
       const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       const float sx = *reinterpret_cast<const LDS_AS float*>(sx_ + 64 * tt);
+      if (GEMM1 && tt + 1 < kTT) {
+        x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + (tt + 1) * 16 * kStride);
+        x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + (tt + 1) * 16 * kStride);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v8i wv = {(int)wf[2 * j].x, (int)wf[2 * j].y, (int)wf[2 * j].z, (int)wf[2 * j].w,
