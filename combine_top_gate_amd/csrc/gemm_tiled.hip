@@ -649,17 +649,38 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
         x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + (tt + 1) * 16 * kStride);
         x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + (tt + 1) * 16 * kStride);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      auto mfma = [&](int j) {
         const v8i wv = {(int)wf[2 * j].x, (int)wf[2 * j].y, (int)wf[2 * j].z, (int)wf[2 * j].w,
                         (int)wf[2 * j + 1].x, (int)wf[2 * j + 1].y, (int)wf[2 * j + 1].z, (int)wf[2 * j + 1].w};
-        const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wv, bv, v4f{0.f, 0.f, 0.f, 0.f}, MFMA_FMT_FP8, MFMA_FMT_FP8, 0, E8M0_ONE, 0, E8M0_ONE);
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, bv, v4f{0.f, 0.f, 0.f, 0.f}, MFMA_FMT_FP8,
+                                                                MFMA_FMT_FP8, 0, E8M0_ONE, 0, E8M0_ONE);
+      };
+      auto promote = [&](int j, const v4f& r) {
         const float sc = swj[GEMM1 ? (j >> 1) : wsel] * sx;
         acc[j][tt][0] = fmaf(r[0], sc, acc[j][tt][0]);
         acc[j][tt][1] = fmaf(r[1], sc, acc[j][tt][1]);
         acc[j][tt][2] = fmaf(r[2], sc, acc[j][tt][2]);
         acc[j][tt][3] = fmaf(r[3], sc, acc[j][tt][3]);
+      };
+      if constexpr (GEMM1) {
+        // two MFMA results in flight: a promotion reads one while the next MFMA runs
+        v4f r0 = mfma(0), r1 = mfma(1);
+        promote(0, r0);
+        r0 = mfma(2);
+        promote(1, r1);
+        r1 = mfma(3);
+        promote(2, r0);
+        promote(3, r1);
+        // the MFMAs and promotions interleaved in this order
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) promote(j, mfma(j));
       }
     }
   };
