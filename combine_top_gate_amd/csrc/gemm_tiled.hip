@@ -633,19 +633,15 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
 #pragma unroll
     for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const LDS_AS u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
     const float swj[2] = {sw_[0], sw_[1]};
-    // GEMM1: token fragments one tile ahead, the LDS reads of tile tt + 1 in flight while
-    // the MFMAs of tile tt run (GEMM2 has no registers to spare for them)
+    // token fragments one tile ahead: the LDS reads of tile tt + 1 are in flight while
+    // the MFMAs of tile tt run
     u32x4 x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0);
     u32x4 x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1);
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      if (!GEMM1 && tt > 0) {
-        x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + tt * 16 * kStride);
-        x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + tt * 16 * kStride);
-      }
       const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       const float sx = *reinterpret_cast<const LDS_AS float*>(sx_ + 64 * tt);
-      if (GEMM1 && tt + 1 < kTT) {
+      if (tt + 1 < kTT) {
         x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + (tt + 1) * 16 * kStride);
         x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + (tt + 1) * 16 * kStride);
       }
@@ -662,26 +658,21 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
         acc[j][tt][2] = fmaf(r[2], sc, acc[j][tt][2]);
         acc[j][tt][3] = fmaf(r[3], sc, acc[j][tt][3]);
       };
-      if constexpr (GEMM1) {
-        // two MFMA results in flight: a promotion reads one while the next MFMA runs
-        v4f r0 = mfma(0), r1 = mfma(1);
-        promote(0, r0);
-        r0 = mfma(2);
-        promote(1, r1);
-        r1 = mfma(3);
-        promote(2, r0);
-        promote(3, r1);
-        // the MFMAs and promotions interleaved in this order
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) promote(j, mfma(j));
-      }
+      // two MFMA results in flight: a promotion reads one while the next MFMA runs
+      v4f r0 = mfma(0), r1 = mfma(1);
+      promote(0, r0);
+      r0 = mfma(2);
+      promote(1, r1);
+      r1 = mfma(3);
+      promote(2, r0);
+      promote(3, r1);
+      // keep that order (MFMA, MFMA, a promotion with its scale product, ...)
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
   };
   // each wait: this wave's loads of the slab have landed (what was issued after it may
