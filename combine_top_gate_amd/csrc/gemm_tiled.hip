@@ -629,14 +629,18 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
     const LDS_AS uint8_t* as_ = L + offsetof(Tiles, a) + st * (BM * kStride);
     const LDS_AS uint8_t* sx_ = L + offsetof(Tiles, sx) + st * (BM * 4) + sxo;
     const LDS_AS float* sw_ = reinterpret_cast<const LDS_AS float*>(L + offsetof(Tiles, sw) + st * 64 * 4);
-    u32x4 wf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wf[i] = *reinterpret_cast<const LDS_AS u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
-    const float swj[2] = {sw_[0], sw_[1]};
-    // token fragments one tile ahead: the LDS reads of tile tt + 1 are in flight while
-    // the MFMAs of tile tt run
+    // the first token tile's fragments, then the weight fragments in the order the
+    // MFMAs use them, so that the first MFMA waits for four reads, not ten
     u32x4 x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0);
     u32x4 x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1);
+    u32x4 wf[8];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wf[i] = *reinterpret_cast<const LDS_AS u32x4*>(ws_ + wfrag_off(i >> 1, i & 1));
+      if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    const float swj[2] = {sw_[0], sw_[1]};
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
       const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
