@@ -235,6 +235,43 @@ __device__ __forceinline__ void compute_slab_a16(v4f (&acc)[4][NT], const u32x4 
   }
 }
 
+// The weight scales of K slab kb for this lane's two weight-scale rows (FP8 weights;
+// MXFP4 weights carry theirs in the MFMA).
+template <int WFMT, bool PACKED>
+__device__ __forceinline__ void slab_wscales(float (&fs)[2], const WSrc<WFMT, PACKED>& ws, int kb) {
+  fs[0] = fs[1] = 1.f;
+  if constexpr (WFMT == MOE_FP8_E4M3) {
+    fs[0] = lane_value(ws.fsv[0], kb);
+    fs[1] = lane_value(ws.fsv[1], kb);
+  }
+}
+
+// The four MFMAs of token tile nt (fragments t0, t1: bytes 16g..16g+15 and 64+16g.. of
+// this lane's token row in the slab) against the wave's weight slab, each promoted into
+// acc with its weight scale times the token scale tsc.
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void mfma_tile(v4f (&acc)[4][NT], const WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws,
+                                          const float (&fs)[2], float tsc, int nt, u32x4 t0, u32x4 t1) {
+  const v8i bv = {(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    v8i av;
+    if constexpr (WeightFmt<WFMT>::kLoads == 2)
+      av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w,
+               (int)s.w[mt][1].x, (int)s.w[mt][1].y, (int)s.w[mt][1].z, (int)s.w[mt][1].w};
+    else
+      av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w, 0, 0, 0, 0};
+    const int ea = kFp4W<WFMT> ? (int)((s.e >> (8 * mt)) & 0xFFu) : E8M0_ONE;
+    const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        av, bv, v4f{0.f, 0.f, 0.f, 0.f}, WeightFmt<WFMT>::kMfmaFmt, MFMA_FMT_FP8, 0, ea, 0, E8M0_ONE);
+    const float sc = (WFMT == MOE_FP8_E4M3 ? fs[ws.fsel[mt]] : 1.f) * tsc;
+    acc[mt][nt][0] = fmaf(r[0], sc, acc[mt][nt][0]);
+    acc[mt][nt][1] = fmaf(r[1], sc, acc[mt][nt][1]);
+    acc[mt][nt][2] = fmaf(r[2], sc, acc[mt][nt][2]);
+    acc[mt][nt][3] = fmaf(r[3], sc, acc[mt][nt][3]);
+  }
+}
+
 // MFMAs of one slab: weights from registers, token fragments from the staged slab tb.
 template <int WFMT, bool PACKED, int NT>
 __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws,
@@ -244,35 +281,15 @@ __device__ __forceinline__ void compute_slab(v4f (&acc)[4][NT], const WSlab<WFMT
     compute_slab_a16<NT>(acc, w, s.e, tb);
     return;
   }
-  float fs[2] = {1.f, 1.f};
-  if constexpr (WFMT == MOE_FP8_E4M3) {
-    fs[0] = lane_value(ws.fsv[0], kb);
-    fs[1] = lane_value(ws.fsv[1], kb);
-  }
+  float fs[2];
+  slab_wscales(fs, ws, kb);
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const uint8_t* tr = tb + (nt * 16 + r16) * TokFmt<false>::kStride + 16 * g4;
     const u32x4 t0 = *reinterpret_cast<const u32x4*>(tr);
     const u32x4 t1 = *reinterpret_cast<const u32x4*>(tr + 64);
-    const v8i bv = {(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      v8i av;
-      if constexpr (WeightFmt<WFMT>::kLoads == 2)
-        av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w,
-                 (int)s.w[mt][1].x, (int)s.w[mt][1].y, (int)s.w[mt][1].z, (int)s.w[mt][1].w};
-      else
-        av = v8i{(int)s.w[mt][0].x, (int)s.w[mt][0].y, (int)s.w[mt][0].z, (int)s.w[mt][0].w, 0, 0, 0, 0};
-      const int ea = kFp4W<WFMT> ? (int)((s.e >> (8 * mt)) & 0xFFu) : E8M0_ONE;
-      const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          av, bv, v4f{0.f, 0.f, 0.f, 0.f}, WeightFmt<WFMT>::kMfmaFmt, MFMA_FMT_FP8, 0, ea, 0, E8M0_ONE);
-      const float sc = (WFMT == MOE_FP8_E4M3 ? fs[ws.fsel[mt]] : 1.f) * s_tsc[kb * (16 * NT) + nt * 16 + r16];
-      acc[mt][nt][0] = fmaf(r[0], sc, acc[mt][nt][0]);
-      acc[mt][nt][1] = fmaf(r[1], sc, acc[mt][nt][1]);
-      acc[mt][nt][2] = fmaf(r[2], sc, acc[mt][nt][2]);
-      acc[mt][nt][3] = fmaf(r[3], sc, acc[mt][nt][3]);
-    }
+    mfma_tile<WFMT, PACKED, NT>(acc, s, ws, fs, s_tsc[kb * (16 * NT) + nt * 16 + r16], nt, t0, t1);
     __builtin_amdgcn_sched_barrier(0);  // one token tile's fragments live at a time
   }
 }
@@ -313,6 +330,61 @@ __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PAC
   for (int kb = 0; kb < KB; kb += 2) {
     step(kb, w0, w1);
     if (kb + 1 < KB) step(kb + 1, w1, w0);
+  }
+}
+
+// The K loop with each lane's token fragments loaded straight from L2 into registers,
+// one slab ahead, in operand order (16 bytes at k = 16g and 64 + 16g of its row per 16-token
+// tile): no LDS staging and no barrier per step, so the four waves of a workgroup run
+// independently.  FP8 activations, at most 3 token tiles (the registers of two fragment
+// sets).  trow[nt]: this lane's token row of tile nt, at k = 0.
+template <int NT>
+using TokFrag = u32x4[NT][2];
+template <int NT>
+__device__ __forceinline__ void load_frag(TokFrag<NT>& f, const uint8_t* const (&trow)[NT], int kb) {
+  const int g4 = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint8_t* r = trow[nt] + (int64_t)kb * 128 + 16 * g4;
+    f[nt][0] = gload16(r);
+    f[nt][1] = gload16(r + 64);
+  }
+}
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void compute_direct(v4f (&acc)[4][NT], const WSlab<WFMT>& s, const WSrc<WFMT, PACKED>& ws,
+                                               const float* s_tsc, int kb, const TokFrag<NT>& f) {
+  float fs[2];
+  slab_wscales(fs, ws, kb);
+  const int r16 = threadIdx.x & 15;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    mfma_tile<WFMT, PACKED, NT>(acc, s, ws, fs, s_tsc[kb * (16 * NT) + nt * 16 + r16], nt, f[nt][0], f[nt][1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+template <int WFMT, bool PACKED, int NT>
+__device__ __forceinline__ void mainloop_direct(v4f (&acc)[4][NT], const WSrc<WFMT, PACKED>& ws,
+                                                const uint8_t* const (&trow)[NT], const float* s_tsc, int KB,
+                                                WSlab<WFMT>& w0) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  TokFrag<NT> fa, fb;
+  load_frag<NT>(fa, trow, 0);
+  // tokens of slab kb + 1 are issued ahead of its weights, so the wait for slab kb's
+  // weights covers its tokens and leaves slab kb + 1 in flight
+  auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& next, const TokFrag<NT>& fc, TokFrag<NT>& fn) {
+    if (kb + 1 < KB) load_frag<NT>(fn, trow, kb + 1);
+    if (kb + 1 < KB) load_wslab(next, ws, kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_direct<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, fc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  WSlab<WFMT> w1;
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, w0, w1, fa, fb);
+    if (kb + 1 < KB) step(kb + 1, w1, w0, fb, fa);
   }
 }
 
@@ -451,7 +523,8 @@ __device__ __forceinline__ void token_row(const GemmArgs& p, const SegTable& t, 
 // row (their results are not stored).
 template <int NT, bool GEMM1, bool A16>
 __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, int g, int M, int m0,
-                                          const float* (&tsc)[NT], int (&orow)[NT]) {
+                                          const float* (&tsc)[NT], int (&orow)[NT],
+                                          const uint8_t* (*trow)[NT] = nullptr) {
   const int r16 = threadIdx.x & 15;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -460,6 +533,7 @@ __device__ __forceinline__ void pass_rows(const GemmArgs& p, const SegTable& t, 
     int r;
     token_row<GEMM1, A16>(p, t, g, m < M ? m : m0, row, tsc[nt], r);
     orow[nt] = m < M ? r : -1;
+    if (trow) (*trow)[nt] = row;
   }
 }
 
@@ -485,7 +559,7 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, const SegTable& t,
 // ------------------------------------------------------------------ GEMM1
 // w0: the pass's first weight slab; issued here unless `issued` (the caller issued it
 // earlier, so that its latency overlaps the caller's own work).
-template <int WFMT, bool PACKED, int NT>
+template <int WFMT, bool PACKED, int NT, bool DIRECT = false>
 __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
                                            int g, int nb, int M, int m0, float (*s_amax)[kMaxTok], float* s_tsc,
                                            uint8_t* s_tok, WSlab<WFMT>& w0, bool issued) {
@@ -499,12 +573,17 @@ __device__ __forceinline__ void gemm1_pass(const GemmArgs& p, const WSrc<WFMT, P
   TokStage<NT, A16> ts;
   if (!issued) load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, true, A16>(p, t, g, M, m0, tsc, orow);
-  stage_rows<NT, true, A16>(p, t, g, M, m0, ts);
+  static_assert(!DIRECT || (!A16 && NT <= 3), "direct token loads: FP8 activations, at most 3 tiles");
+  const uint8_t* trow[NT];
+  pass_rows<NT, true, A16>(p, t, g, M, m0, tsc, orow, &trow);
+  if constexpr (!DIRECT) stage_rows<NT, true, A16>(p, t, g, M, m0, ts);
   if constexpr (!A16) stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
-  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
+  if constexpr (DIRECT)
+    mainloop_direct<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, KB, w0);
+  else
+    mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
 
   if constexpr (A16) {
     // SwiGLU, h stored bf16: this lane holds rows rb + 16t + 4*g4 + i of token column
@@ -587,6 +666,12 @@ struct DispatchPrologue {
   }
 };
 
+// The one-tile passes of the small-batch kernels (at most two token tiles per pass,
+// FP8 activations) load their token fragments straight into registers; in the kernels
+// for larger batches such passes are rare and the staged loop alone measured faster.
+template <int NTMAX, int WFMT>
+constexpr bool kDirect1 = NTMAX == 2 && !kA16<WFMT>;
+
 template <int NTMAX, int WFMT, bool PACKED, class Prologue = NoPrologue>
 __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item, float (*s_amax)[kMaxTok],
                                            float* s_tsc, uint8_t* s_tok, SegTable& seg,
@@ -659,7 +744,7 @@ __device__ __forceinline__ void gemm1_item(const GemmArgs& p, int g, int nb_item
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     const bool issued = pro && m0 == mb;
     switch (nt) {
-      case 1: gemm1_pass<WFMT, PACKED, 1>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
+      case 1: gemm1_pass<WFMT, PACKED, 1, kDirect1<NTMAX, WFMT>>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
       case 2: if constexpr (NTMAX >= 2) gemm1_pass<WFMT, PACKED, 2>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
       case 3: if constexpr (NTMAX >= 3) gemm1_pass<WFMT, PACKED, 3>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
       case 4: if constexpr (NTMAX >= 4) gemm1_pass<WFMT, PACKED, 4>(p, ws, seg, g, nb, me, m0, s_amax, s_tsc, s_tok, w0, issued); break;
@@ -699,7 +784,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs 
 }
 
 // ------------------------------------------------------------------ GEMM2
-template <int WFMT, bool PACKED, int NT>
+template <int WFMT, bool PACKED, int NT, bool DIRECT = false>
 __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
                                            int g, int rb, bool active, int K, int M, int m0, float* s_tsc,
                                            uint8_t* s_tok) {
@@ -713,13 +798,18 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
   WSlab<WFMT> w0;
   load_wslab(w0, ws, 0);  // the first weight slab is in flight during the pass setup
   __builtin_amdgcn_sched_barrier(0);
-  pass_rows<NT, false, A16>(p, t, g, M, m0, tsc, orow);
-  stage_rows<NT, false, A16>(p, t, g, M, m0, ts);
+  static_assert(!DIRECT || (!A16 && NT <= 3), "direct token loads: FP8 activations, at most 3 tiles");
+  const uint8_t* trow[NT];
+  pass_rows<NT, false, A16>(p, t, g, M, m0, tsc, orow, &trow);
+  if constexpr (!DIRECT) stage_rows<NT, false, A16>(p, t, g, M, m0, ts);
   if constexpr (!A16) stage_token_scales<NT>(s_tsc, tsc, KB);
   __syncthreads();
   v4f acc[4][NT];
   // a wave past a ragged end of H repeats the last tile's rows and stores nothing
-  mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
+  if constexpr (DIRECT)
+    mainloop_direct<WFMT, PACKED, NT>(acc, ws, trow, s_tsc, KB, w0);
+  else
+    mainloop<WFMT, PACKED, NT>(acc, ws, ts, s_tok, s_tsc, KB, w0);
   __syncthreads();  // s_tsc is reused by the next pass
   if (!active) return;
 #pragma unroll
@@ -787,7 +877,7 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
   for (int m0 = mb; m0 < me; m0 += 16 * NTMAX) {
     const int nt = min(NTMAX, (me - m0 + 15) >> 4);
     switch (nt) {
-      case 1: gemm2_pass<WFMT, PACKED, 1>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
+      case 1: gemm2_pass<WFMT, PACKED, 1, kDirect1<NTMAX, WFMT>>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
       case 2: if constexpr (NTMAX >= 2) gemm2_pass<WFMT, PACKED, 2>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
       case 3: if constexpr (NTMAX >= 3) gemm2_pass<WFMT, PACKED, 3>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
       case 4: if constexpr (NTMAX >= 4) gemm2_pass<WFMT, PACKED, 4>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;

@@ -109,6 +109,9 @@ def test_packed_weights_give_identical_output(name, over):
 
 @pytest.mark.parametrize("name,over", [
     ("decode128_fp8", {}),
+    # one token tile per expert: the small-batch kernels load token fragments into
+    # registers, the kernels for three or more tiles stage them in LDS
+    ("decode8_fp8", {}),
     ("decode256_mxfp4_shared", dict(S=3, T_s=11, H=384, I=256, E=5, k=2, shared_I=128, seed=53)),
     ("prefill4096_zipf_fp8", dict(S=4, T_s=64, H=512, I=256, E=16, k=4, seed=54)),
     # W4A16 runs two kernels whatever the persistent option says
@@ -121,7 +124,8 @@ def test_gemm_schedules_give_identical_output(name, over):
     moe, d = run(inp, packed=True)
     ref = d.out.clone()
     for opt, val in [(binding.MOE_OPT_QUEUE, 2), (binding.MOE_OPT_QUEUE, 1), (binding.MOE_OPT_TOKEN_TILES, 2),
-                     (binding.MOE_OPT_TOKEN_TILES, 4), (binding.MOE_OPT_PERSISTENT_GEMM, 0)]:
+                     (binding.MOE_OPT_TOKEN_TILES, 3), (binding.MOE_OPT_TOKEN_TILES, 4),
+                     (binding.MOE_OPT_PERSISTENT_GEMM, 0)]:
         moe.set_option(opt, val)
         d.out.zero_()
         moe.run(d)
