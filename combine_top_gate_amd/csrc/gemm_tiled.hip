@@ -42,6 +42,14 @@ constexpr int kALd = kAPieces / kThreads;  // 16-byte token pieces per thread pe
 constexpr int kWLd = kWPieces / kThreads;  // 16-byte weight pieces per thread per slab
 constexpr int kSxWaves = BM / 64;          // waves that load the token scales
 constexpr int kLoadsPerSlab = kALd + kWLd + 1;
+// per item height: TT 16-row token tiles per wave (kTT, or kTT / 2 for a half-height
+// item of BM / 2 rows): token pieces per thread, waves loading token scales, DMAs per wave
+template <int TT>
+constexpr int kALdOf = TT * 32 * 8 / kThreads;
+template <int TT>
+constexpr int kSxWavesOf = TT * 32 / 64;
+template <int TT>
+constexpr int kLoadsOf = kALdOf<TT> + kWLd + 1;
 static_assert(kSxWaves < kThreads / 64, "a wave is left for the weight scales");
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const GLOBAL u32x4*)p; }
@@ -240,8 +248,9 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <bool GEMM1, bool PK>
+template <bool GEMM1, bool PK, int TT = kTT>
 __device__ __forceinline__ TileSrc<PK> make_src(const GemmArgs& p, int g, int nb, const int* rows, const Tiles& T) {
+  constexpr int nA = kALdOf<TT>;
   const BatchDims& d = p.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool shared = g == d.E;
@@ -250,8 +259,8 @@ __device__ __forceinline__ TileSrc<PK> make_src(const GemmArgs& p, int g, int nb
   const int KB = K >> 7;
   TileSrc<PK> src;
 #pragma unroll
-  for (int i = 0; i < kALd; ++i) {
-    const int q = (wave * kALd + i) * 64 + lane;
+  for (int i = 0; i < nA; ++i) {
+    const int q = (wave * nA + i) * 64 + lane;
     const int r = q >> 3;
     const int c = (q & 7) ^ ((r >> 1) & 7);
     const int wr = rows[r];
@@ -298,7 +307,7 @@ __device__ __forceinline__ TileSrc<PK> make_src(const GemmArgs& p, int g, int nb
   // into sdummy
   const float* ws0 = WS + (int64_t)(GEMM1 ? nb : min(2 * nb, (d.H >> 7) - 1)) * KB;
   const float* ws1 = WS + (int64_t)(GEMM1 ? (inter >> 7) + nb : min(2 * nb + 1, (d.H >> 7) - 1)) * KB;
-  if (wave < kSxWaves) {
+  if (wave < kSxWavesOf<TT>) {
     const int wr = rows[64 * wave + lane];
     if (GEMM1 && shared) {
       const int s = wr / d.T_s, tt = wr - s * d.T_s;
@@ -312,15 +321,16 @@ __device__ __forceinline__ TileSrc<PK> make_src(const GemmArgs& p, int g, int nb
   return src;
 }
 
-// The DMAs of K slab kb into ring stage st (every wave issues kLoadsPerSlab of them).
-template <bool PK>
+// The DMAs of K slab kb into ring stage st (every wave issues kLoadsOf<TT> of them).
+template <bool PK, int TT = kTT>
 __device__ __forceinline__ void issue_slab(const TileSrc<PK>& src, int kb, int st, Tiles& T) {
+  constexpr int nA = kALdOf<TT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // LDS addresses as plain offsets from the tile buffers' base (uniform, scalar registers)
   const uint32_t t0 = __builtin_amdgcn_readfirstlane(lds_off(&T));
 #pragma unroll
-  for (int i = 0; i < kALd; ++i)
-    dma16(src.a[i] + (int64_t)kb * 128, t0 + offsetof(Tiles, a) + st * (BM * kStride) + (wave * kALd + i) * 1024);
+  for (int i = 0; i < nA; ++i)
+    dma16(src.a[i] + (int64_t)kb * 128, t0 + offsetof(Tiles, a) + st * (BM * kStride) + (wave * nA + i) * 1024);
   const uint32_t wdst = t0 + offsetof(Tiles, w) + st * (BN * kStride) + wave * kWLd * 1024;
   if constexpr (PK) {
     const uint8_t* wb = src.w[0] + (int64_t)kb * 8192;  // uniform
@@ -331,7 +341,7 @@ __device__ __forceinline__ void issue_slab(const TileSrc<PK>& src, int kb, int s
 #pragma unroll
     for (int i = 0; i < kWLd; ++i) dma16(src.w[i] + (int64_t)kb * 128, wdst + i * 1024);
   }
-  const uint32_t sdst = wave < kSxWaves ? t0 + offsetof(Tiles, sx) + (st * BM + 64 * wave) * 4
+  const uint32_t sdst = wave < kSxWavesOf<TT> ? t0 + offsetof(Tiles, sx) + (st * BM + 64 * wave) * 4
                         : wave == kSxWaves ? t0 + offsetof(Tiles, sw) + st * 64 * 4
                                            : t0 + offsetof(Tiles, sdummy);
   dma4(src.s + kb, sdst);
@@ -576,11 +586,11 @@ __device__ __forceinline__ int item_kb(const GemmArgs& p, int g) {
 
 // Issues an item's slab 0 into stage 0 and (when it has more) slab 1 into stage 1; the
 // ring must be idle.
-template <bool GEMM1, bool PK>
+template <bool GEMM1, bool PK, int TT>
 __device__ __forceinline__ void issue_first(const GemmArgs& p, const Item& it, const int* rows, Tiles& T) {
-  const TileSrc<PK> src = make_src<GEMM1, PK>(p, it.g, it.nb, rows, T);
-  issue_slab<PK>(src, 0, 0, T);
-  if (item_kb<GEMM1>(p, it.g) > 1) issue_slab<PK>(src, 1, 1, T);
+  const TileSrc<PK> src = make_src<GEMM1, PK, TT>(p, it.g, it.nb, rows, T);
+  issue_slab<PK, TT>(src, 0, 0, T);
+  if (item_kb<GEMM1>(p, it.g) > 1) issue_slab<PK, TT>(src, 1, 1, T);
 }
 
 // This wave's weight tiles: (GEMM1) gate rows wn*32 + 16*j and up rows 128 + wn*32 +
@@ -596,9 +606,10 @@ __device__ __forceinline__ int wave_row(int wn, int j) {
 // placeholders before the first item).  From step 1 on, step kb issues slab kb + 1 into
 // the stage read at step kb - 1.  Steps 0 and 1 are written out, so that every wait
 // count is a constant and the loop itself is one uniform body.
-template <bool GEMM1, bool PK>
-__device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& src, Tiles& T, int KB) {
+template <bool GEMM1, bool PK, int TT>
+__device__ __forceinline__ void kloop16(v4f (&acc)[4][TT], const TileSrc<PK>& src, Tiles& T, int KB) {
   constexpr bool t_packed = PK;
+  constexpr int TR = 16 * TT;  // token rows per wave
   constexpr int S = kEpiStores<GEMM1>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -610,7 +621,7 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
   const int r0 = wave_row<GEMM1>(wn, 0);
   const int w0 = t_packed ? wn * 8192 + lane * 16 : swz(r0 + r16, g4);
   const int w1 = t_packed ? w0 + 1024 : swz(r0 + r16, g4 + 4);
-  const int a0 = swz(wm * (BM / 2) + r16, g4), a1 = swz(wm * (BM / 2) + r16, g4 + 4);
+  const int a0 = swz(wm * TR + r16, g4), a1 = swz(wm * TR + r16, g4 + 4);
   auto wfrag_off = [&](int j, int h) {  // weight tile j, half h
     const int base = h ? w1 : w0;
     return t_packed ? base + 2 * j * 1024 : base + (wave_row<GEMM1>(wn, j) - r0) * kStride;
@@ -618,12 +629,12 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TT; ++tt) acc[j][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // LDS reads through an LDS-space pointer: per-lane offsets plus constants the LDS
   // instructions take as immediates
   const LDS_AS uint8_t* L = (const LDS_AS uint8_t*)(const uint8_t*)(&T);
-  const int sxo = (wm * (BM / 2) + r16) * 4;
+  const int sxo = (wm * TR + r16) * 4;
   auto compute = [&](int st) {
     const LDS_AS uint8_t* ws_ = L + offsetof(Tiles, w) + st * (BN * kStride);
     const LDS_AS uint8_t* as_ = L + offsetof(Tiles, a) + st * (BM * kStride);
@@ -642,10 +653,10 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
     }
     const float swj[2] = {sw_[0], sw_[1]};
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
       const v8i bv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       const float sx = *reinterpret_cast<const LDS_AS float*>(sx_ + 64 * tt);
-      if (tt + 1 < kTT) {
+      if (tt + 1 < TT) {
         x0 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a0 + (tt + 1) * 16 * kStride);
         x1 = *reinterpret_cast<const LDS_AS u32x4*>(as_ + a1 + (tt + 1) * 16 * kStride);
       }
@@ -682,17 +693,17 @@ __device__ __forceinline__ void kloop16(v4f (&acc)[4][kTT], const TileSrc<PK>& s
   // each wait: this wave's loads of the slab have landed (what was issued after it may
   // stay in flight), then the barrier: every wave's have
   if (KB > 1)
-    wait_barrier<kLoadsPerSlab + S>();
+    wait_barrier<kLoadsOf<TT> + S>();
   else
     wait_barrier<S>();
   compute(0);
   if (KB == 1) return;
   wait_barrier<S>();
-  if (KB > 2) issue_slab<PK>(src, 2, 0, T);
+  if (KB > 2) issue_slab<PK, TT>(src, 2, 0, T);
   compute(1);
   for (int kb = 2; kb < KB; ++kb) {
     wait_barrier<0>();
-    if (kb + 1 < KB) issue_slab<PK>(src, kb + 1, (kb + 1) & 1, T);
+    if (kb + 1 < KB) issue_slab<PK, TT>(src, kb + 1, (kb + 1) & 1, T);
     compute(kb & 1);
   }
 }
@@ -708,9 +719,10 @@ __device__ __forceinline__ void placeholder_stores(int* plan) {
 
 // The epilogue of an item: exactly kEpiStores<GEMM1> store instructions per wave.  Lane
 // (g4, r16) holds weight rows wave_row(wn, j) + 4*g4 + i of token wm*(BM/2) + 16*tt + r16.
-template <bool GEMM1>
-__device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, const int* rows, v4f (&acc)[4][kTT],
+template <bool GEMM1, int TT>
+__device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, const int* rows, v4f (&acc)[4][TT],
                                            Tiles& T, int* plan) {
+  constexpr int TR = 16 * TT;  // token rows per wave
   const BatchDims& d = p.d;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -721,7 +733,7 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, co
   if constexpr (GEMM1) {
     // SwiGLU in place: acc[j] (gate, j = 0, 1) becomes h; acc[2 + j] (up) is then dead
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
       float mx = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -733,13 +745,13 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, co
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (g4 == 0) T.amax[wn][wm * (BM / 2) + 16 * tt + r16] = mx;
+      if (g4 == 0) T.amax[wn][wm * TR + 16 * tt + r16] = mx;
     }
     lds_barrier();
     const int hsc_stride = d.hstride >> 7;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      const int tr = wm * (BM / 2) + 16 * tt + r16;
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tr = wm * TR + 16 * tt + r16;
       const bool ok = it.m0 + tr < it.M;
       const int orow = shared ? d.R + rows[tr] : rows[tr];
       const float amax = fmaxf(fmaxf(T.amax[0][tr], T.amax[1][tr]), fmaxf(T.amax[2][tr], T.amax[3][tr]));
@@ -761,12 +773,15 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, co
                                              : trash;
       store32<0>(sp, __float_as_uint(sc));
     }
+    // a half-height item's stores are padded to the full count
+#pragma unroll
+    for (int i = 0; i < 3 * (kTT - TT); ++i) store32(trash, 0u);
   } else {
     // this wave's 64 columns are all inside H or all past it (H is a multiple of 128)
     const bool col_ok = it.nb * BN + wn * 64 < d.H;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      const int tr = wm * (BM / 2) + 16 * tt + r16;
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tr = wm * TR + 16 * tt + r16;
       const bool ok = col_ok && it.m0 + tr < it.M;
       // columns nb*BN + wn*64 + 16 j + 4 g4 .. + 3 (j = 0..3: 32 bytes apart)
       uint8_t* yp = ok ? reinterpret_cast<uint8_t*>(p.y + (int64_t)rows[tr] * d.H + it.nb * BN + wn * 64 + 4 * g4)
@@ -780,11 +795,48 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, co
       store64<64>(yp, v[2]);
       store64<96>(yp, v[3]);
     }
+#pragma unroll
+    for (int i = 0; i < 4 * (kTT - TT); ++i) store32(trash, 0u);
   }
 }
 
-// The persistent loop of the default path: items from the queues; the next item's first
-// two slabs are issued before this item's epilogue.
+// An item whose token tile holds at most BM / 2 rows (an expert's ragged last tile) runs
+// half-height: its rows split over all eight waves (64 each, TT = kTT / 2), so that it
+// takes about half a full item's time instead of leaving half the waves' MFMAs idle.
+__device__ __forceinline__ bool half_item(const Item& it) { return it.M - it.m0 <= BM / 2; }
+
+// One item of the persistent loop, TT token tiles per wave: its K loop, then the next
+// item from the queues, whose row table is built and first two slabs issued before this
+// item's epilogue.  Returns false (after the epilogue) when the queues are exhausted.
+template <bool GEMM1, bool PK, int TT>
+__device__ __forceinline__ bool step16(const TiledArgs& t, Tiles& T, int& q, int& left, Item& it, int& sb) {
+  const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
+  v4f acc[4][TT];
+  {
+    const TileSrc<PK> src = make_src<GEMM1, PK, TT>(p, it.g, it.nb, T.rows[sb], T);
+    kloop16<GEMM1, PK, TT>(acc, src, T, item_kb<GEMM1>(p, it.g));
+  }
+  Item nx;
+  // its barriers also end every wave's reads of the ring
+  const bool more = next_item<GEMM1>(t, T, q, left, nx);
+  if (more) {
+    segments(p, nx.g, T.seg);
+    __syncthreads();
+    row_table<GEMM1>(p, nx.g, nx.M, nx.m0, T.seg, T.rows[sb ^ 1]);
+    if (half_item(nx))
+      issue_first<GEMM1, PK, kTT / 2>(p, nx, T.rows[sb ^ 1], T);
+    else
+      issue_first<GEMM1, PK, kTT>(p, nx, T.rows[sb ^ 1], T);
+  }
+  epilogue16<GEMM1, TT>(p, it, T.rows[sb], acc, T, t.plan);
+  if (more) {
+    it = nx;
+    sb ^= 1;
+  }
+  return more;
+}
+
+// The persistent loop of the default path.
 template <bool GEMM1, bool PK>
 __device__ void run16(const TiledArgs& t, Tiles& T) {
   const GemmArgs& p = GEMM1 ? t.g1 : t.g2;
@@ -795,27 +847,15 @@ __device__ void run16(const TiledArgs& t, Tiles& T) {
   segments(p, it.g, T.seg);
   __syncthreads();
   row_table<GEMM1>(p, it.g, it.M, it.m0, T.seg, T.rows[sb]);
-  issue_first<GEMM1, PK>(p, it, T.rows[sb], T);
+  if (half_item(it))
+    issue_first<GEMM1, PK, kTT / 2>(p, it, T.rows[sb], T);
+  else
+    issue_first<GEMM1, PK, kTT>(p, it, T.rows[sb], T);
   placeholder_stores<GEMM1>(t.plan);
   for (;;) {
-    v4f acc[4][kTT];
-    {
-      const TileSrc<PK> src = make_src<GEMM1, PK>(p, it.g, it.nb, T.rows[sb], T);
-      kloop16<GEMM1, PK>(acc, src, T, item_kb<GEMM1>(p, it.g));
-    }
-    Item nx;
-    // its barriers also end every wave's reads of the ring
-    const bool more = next_item<GEMM1>(t, T, q, left, nx);
-    if (more) {
-      segments(p, nx.g, T.seg);
-      __syncthreads();
-      row_table<GEMM1>(p, nx.g, nx.M, nx.m0, T.seg, T.rows[sb ^ 1]);
-      issue_first<GEMM1, PK>(p, nx, T.rows[sb ^ 1], T);
-    }
-    epilogue16<GEMM1>(p, it, T.rows[sb], acc, T, t.plan);
+    const bool more = half_item(it) ? step16<GEMM1, PK, kTT / 2>(t, T, q, left, it, sb)
+                                    : step16<GEMM1, PK, kTT>(t, T, q, left, it, sb);
     if (!more) break;
-    it = nx;
-    sb ^= 1;
   }
 }
 
