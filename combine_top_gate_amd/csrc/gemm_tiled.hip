@@ -594,7 +594,7 @@ __device__ __forceinline__ void issue_first(const GemmArgs& p, const Item& it, c
 }
 
 // This wave's weight tiles: (GEMM1) gate rows wn*32 + 16*j and up rows 128 + wn*32 +
-// 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j.  Its token tiles: wm*(BM/2) + 16*tt.
+// 16*j (j = 0, 1); (GEMM2) rows wn*64 + 16*j.  Its token tiles: wm*16*TT + 16*tt (TT tiles per wave).
 template <bool GEMM1>
 __device__ __forceinline__ int wave_row(int wn, int j) {
   return GEMM1 ? ((j >> 1) * 128 + wn * 32 + 16 * (j & 1)) : (wn * 64 + 16 * j);
@@ -718,7 +718,7 @@ __device__ __forceinline__ void placeholder_stores(int* plan) {
 }
 
 // The epilogue of an item: exactly kEpiStores<GEMM1> store instructions per wave.  Lane
-// (g4, r16) holds weight rows wave_row(wn, j) + 4*g4 + i of token wm*(BM/2) + 16*tt + r16.
+// (g4, r16) holds weight rows wave_row(wn, j) + 4*g4 + i of token wm*16*TT + 16*tt + r16.
 template <bool GEMM1, int TT>
 __device__ __forceinline__ void epilogue16(const GemmArgs& p, const Item& it, const int* rows, v4f (&acc)[4][TT],
                                            Tiles& T, int* plan) {
