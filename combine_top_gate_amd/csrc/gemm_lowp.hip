@@ -316,20 +316,35 @@ __device__ __forceinline__ void mainloop(v4f (&acc)[4][NT], const WSrc<WFMT, PAC
   load_tok<NT, A16>(tv, ts, 0);
   store_tok<NT, A16>(s_tok, tv, ts);
   __syncthreads();
-  // one K step: `next` receives the weights of slab kb + 1
+  // one K step that loads slab kb + 1 (`next` receives its weights)
   auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& next) {
-    if (kb + 1 < KB) load_tok<NT, A16>(tv, ts, kb + 1);
-    if (kb + 1 < KB) load_wslab(next, ws, kb + 1);
+    load_tok<NT, A16>(tv, ts, kb + 1);
+    load_wslab(next, ws, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute_slab<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, s_tok + (kb & 1) * BUF);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < KB) store_tok<NT, A16>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
+    store_tok<NT, A16>(s_tok + ((kb + 1) & 1) * BUF, tv, ts);
     __syncthreads();
   };
+  // the last step: nothing left to load
+  auto last = [&](int kb, WSlab<WFMT>& cur) {
+    compute_slab<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, s_tok + (kb & 1) * BUF);
+    __syncthreads();
+  };
+  // The loop body holds no condition around a load: at a join of paths with and without
+  // the next slab's loads in flight, the compiler's wait counts would have to hold for
+  // both, and so would wait for those loads inside the step meant to overlap them.
   WSlab<WFMT> w1;
-  for (int kb = 0; kb < KB; kb += 2) {
+  int kb = 0;
+  for (; kb + 2 < KB; kb += 2) {
     step(kb, w0, w1);
-    if (kb + 1 < KB) step(kb + 1, w1, w0);
+    step(kb + 1, w1, w0);
+  }
+  if (kb + 2 == KB) {
+    step(kb, w0, w1);
+    last(kb + 1, w1);
+  } else {
+    last(kb, w0);
   }
 }
 
@@ -375,16 +390,24 @@ __device__ __forceinline__ void mainloop_direct(v4f (&acc)[4][NT], const WSrc<WF
   // tokens of slab kb + 1 are issued ahead of its weights, so the wait for slab kb's
   // weights covers its tokens and leaves slab kb + 1 in flight
   auto step = [&](int kb, WSlab<WFMT>& cur, WSlab<WFMT>& next, const TokFrag<NT>& fc, TokFrag<NT>& fn) {
-    if (kb + 1 < KB) load_frag<NT>(fn, trow, kb + 1);
-    if (kb + 1 < KB) load_wslab(next, ws, kb + 1);
+    load_frag<NT>(fn, trow, kb + 1);
+    load_wslab(next, ws, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute_direct<WFMT, PACKED, NT>(acc, cur, ws, s_tsc, kb, fc);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // no condition around a load inside the loop (see mainloop)
   WSlab<WFMT> w1;
-  for (int kb = 0; kb < KB; kb += 2) {
+  int kb = 0;
+  for (; kb + 2 < KB; kb += 2) {
     step(kb, w0, w1, fa, fb);
-    if (kb + 1 < KB) step(kb + 1, w1, w0, fb, fa);
+    step(kb + 1, w1, w0, fb, fa);
+  }
+  if (kb + 2 == KB) {
+    step(kb, w0, w1, fa, fb);
+    compute_direct<WFMT, PACKED, NT>(acc, w1, ws, s_tsc, kb + 1, fb);
+  } else {
+    compute_direct<WFMT, PACKED, NT>(acc, w0, ws, s_tsc, kb, fa);
   }
 }
 
