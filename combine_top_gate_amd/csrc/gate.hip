@@ -22,6 +22,17 @@
 // split into ks contiguous slices over workgroups, so that a small batch still spreads
 // over every CU; each workgroup writes its slice's partial tile to a workspace.
 //
+// k_router_lds (many tokens, H a multiple of 128): a workgroup owns 64 tokens x 64
+// experts and a K slice.  128-deep K chunks of both operands are staged in LDS, each row
+// padded to 272 bytes, double-buffered; the loads (16 contiguous bytes per thread and
+// piece, whole 256-byte rows per 16 threads) run two chunks ahead in two register sets,
+// and a chunk is written to the free buffer after the current one's MFMAs, one barrier
+// per chunk.  Four waves of 32 tokens x 32 experts (2 x 2 MFMA tiles each); each wave
+// chains its whole K slice in one accumulator.  The fragment
+// loads of the other two kernels, 16 bytes from each of 16 rows per instruction and every
+// row re-read by each expert block, bound them at a few percent of the MFMA rate once the
+// batch has thousands of tokens.
+//
 // k_topk: one wave (and workgroup) per token, E <= 256 logits, 4 per lane (added up from the ks partial
 // sums in slice order first, when there are several).  The k-th largest logit is
 // found exactly by a radix select over order-preserving 32-bit keys (one ballot per
@@ -262,9 +273,166 @@ __global__ __launch_bounds__(64) void k_topk(TopkArgs a) {
   }
 }
 
+constexpr int kRlRows = 64;                 // tokens, and experts, per workgroup
+constexpr int kRlK = 128;                   // K elements per staged chunk
+constexpr int kRlStride = kRlK * 2 + 16;    // bytes per staged row
+constexpr int kRlPieces = kRlRows * kRlK * 2 / 16 / 256;  // 16-byte pieces per thread and operand
+struct RlSmem {
+  uint8_t x[2][kRlRows * kRlStride];
+  uint8_t w[2][kRlRows * kRlStride];
+};
+
+// partial[slice][t][e] over K chunks [nch * slice / ks, nch * (slice + 1) / ks) (nch = H / 128).
+__global__ __launch_bounds__(256) void k_router_lds(RouterSplitArgs a) {
+  __shared__ __align__(16) RlSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // XCD x takes a contiguous run of workgroups, expert blocks fastest, so that a token
+  // block's rows are fetched into one XCD's L2 for all its expert blocks
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int n = gx * gy * gridDim.z, b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xcd = b & 7, per = n >> 3, extra = n & 7;
+  const int L = xcd * per + min(xcd, extra) + (b >> 3);
+  const int eb = L % gx, rest = L / gx;
+  const int e0 = eb * kRlRows, t0 = (rest % gy) * kRlRows, slice = rest / gy;
+  const int nch = a.H / kRlK;
+  const int c_begin = (int)((int64_t)nch * slice / a.ks), c_end = (int)((int64_t)nch * (slice + 1) / a.ks);
+  // this thread's pieces: piece q = tid + 256 i is 16 bytes at column 16 (q % 16) of row q / 16
+  const uint16_t* xs[kRlPieces];
+  const uint16_t* ws[kRlPieces];
+  int so[kRlPieces];
+#pragma unroll
+  for (int i = 0; i < kRlPieces; ++i) {
+    const int q = tid + 256 * i, row = q >> 4, col = q & 15;
+    xs[i] = a.x + (int64_t)min(t0 + row, a.T - 1) * a.H + 8 * col;
+    ws[i] = a.wr + (int64_t)min(e0 + row, a.E - 1) * a.H + 8 * col;
+    so[i] = row * kRlStride + 16 * col;
+  }
+  // two register sets of staged pieces: chunk j of the slice (j >= 1) travels in set j & 1
+  u32x4 xv[2][kRlPieces], wv[2][kRlPieces];
+  auto load = [&](int set, int j) {
+    const int64_t off = (int64_t)(c_begin + j) * kRlK;
+#pragma unroll
+    for (int i = 0; i < kRlPieces; ++i) {
+      xv[set][i] = gload16(xs[i] + off);
+      wv[set][i] = gload16(ws[i] + off);
+    }
+  };
+  auto store = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < kRlPieces; ++i) {
+      *reinterpret_cast<u32x4*>(sm.x[buf] + so[i]) = xv[set][i];
+      *reinterpret_cast<u32x4*>(sm.w[buf] + so[i]) = wv[set][i];
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;  // token half, expert half
+  v4f acc[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[j][u] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+    const uint8_t* xb = sm.x[buf] + (wm * 32 + r16) * kRlStride + 16 * g4;
+    const uint8_t* wb = sm.w[buf] + (wn * 32 + r16) * kRlStride + 16 * g4;
+#pragma unroll
+    for (int s = 0; s < kRlK / 32; ++s) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fa[j] = *reinterpret_cast<const u32x4*>(wb + j * 16 * kRlStride + 64 * s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) fb[u] = *reinterpret_cast<const u32x4*>(xb + u * 16 * kRlStride + 64 * s);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          acc[j][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8s(fa[j]), as_v8s(fb[u]), acc[j][u], 0, 0, 0);
+    }
+  };
+  const int nc = c_end - c_begin;
+  if (nc >= 5) {
+    // chunks two ahead: at step j, LDS buffer j & 1 holds chunk j, set (j + 1) & 1 chunk
+    // j + 1 (stored after this step's MFMAs) and set j & 1 chunk j + 2 (in flight); the
+    // freed set then takes chunk j + 3.  No condition around a load inside the loop: the
+    // last four steps are peeled.
+    load(0, 0);
+    store(0, 0);
+    __syncthreads();
+    load(1, 1);
+    load(0, 2);
+    auto step = [&](int j, int set) {  // set = (j + 1) & 1
+      compute(j & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      store(set, (j + 1) & 1);
+      __syncthreads();
+    };
+    int j = 0;
+    for (; j + 4 < nc; j += 2) {
+      step(j, 1);
+      load(1, j + 3);
+      __builtin_amdgcn_sched_barrier(0);  // the loads right after the barrier
+      step(j + 1, 0);
+      load(0, j + 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // j is even; the steps j .. nc - 1 remain (1 to 4 of them), chunk j + 3 still to load
+    // when it exists
+    const int r = nc - j;
+    if (r == 4) {
+      step(j, 1);
+      load(1, j + 3);
+      step(j + 1, 0);
+      step(j + 2, 1);
+      compute((j + 3) & 1);
+    } else if (r == 3) {
+      step(j, 1);
+      step(j + 1, 0);
+      compute((j + 2) & 1);
+    } else if (r == 2) {
+      step(j, 1);
+      compute((j + 1) & 1);
+    } else {
+      compute(j & 1);
+    }
+  } else if (nc > 0) {
+    // a few chunks: one ahead
+    load(0, 0);
+    store(0, 0);
+    __syncthreads();
+    for (int j = 0; j < nc; ++j) {
+      if (j + 1 < nc) load(1, j + 1);
+      compute(j & 1);
+      if (j + 1 < nc) {
+        store(1, (j + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+  float* out = a.partial + (int64_t)slice * a.T * a.E;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int er = e0 + wn * 32 + 16 * j + 4 * g4 + i, tc = t0 + wm * 32 + 16 * u + r16;
+        if (er < a.E && tc < a.T) out[(int64_t)tc * a.E + er] = acc[j][u][i];
+      }
+}
+
 }  // namespace
 
+// The LDS-tiled router from this many tokens on (H a multiple of 128).
+constexpr int kRouterLdsMinT = 256;
+static bool router_lds(int T, int H) { return T >= kRouterLdsMinT && H % kRlK == 0; }
+static int rl_tiles(int T, int E) { return ((E + kRlRows - 1) / kRlRows) * ((T + kRlRows - 1) / kRlRows); }
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
+  if (router_lds(a.T, a.H)) {
+    const RouterSplitArgs r{a.x, a.wr, a.logits, a.T, a.H, a.E, 1};
+    hipLaunchKernelGGL(k_router_lds, dim3((a.E + kRlRows - 1) / kRlRows, (a.T + kRlRows - 1) / kRlRows, 1), dim3(256),
+                       0, st, r);
+    return hipGetLastError();
+  }
   // Enough workgroups to cover the CUs with 16-token tiles when T is small; wider token
   // tiles cut the L2 re-reads of the router weights once there are tokens to spare.
   const int eb = (a.E + 15) / 16;
@@ -276,6 +444,12 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
 }
 
 int gate_split(int T, int H, int E) {
+  if (router_lds(T, H)) {
+    // about 256 workgroups, within the no-allocation scratch (ks x T x E fp32 partial
+    // sums, 4 MiB: ks x T <= 4096 at 256 experts)
+    const int want = (256 + rl_tiles(T, E) - 1) / rl_tiles(T, E);
+    return std::max(1, std::min({want, 4096 / T, kGateMaxSplit, H / kRlK}));
+  }
   // Token tiles of up to 128 tokens; split K until about 256 workgroups are in flight, with
   // at least 8 K steps (two per wave) in every slice.  Measured on MI355X (H 7168, 256
   // experts, gate call in us), against every fixed split of 1-16: the rule's choice is the
@@ -288,6 +462,11 @@ int gate_split(int T, int H, int E) {
 }
 
 hipError_t launch_router_split(const RouterSplitArgs& a, hipStream_t st) {
+  if (router_lds(a.T, a.H)) {
+    hipLaunchKernelGGL(k_router_lds, dim3((a.E + kRlRows - 1) / kRlRows, (a.T + kRlRows - 1) / kRlRows, a.ks),
+                       dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const int eb = (a.E + 15) / 16;
   if (a.T > 64)
     hipLaunchKernelGGL((k_router_split<8, 3>), dim3(eb, (a.T + 127) / 128, a.ks), dim3(256), 0, st, a);

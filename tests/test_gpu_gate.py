@@ -91,14 +91,20 @@ def router_case(T, H, E, seed):
     x, wr = codecs.bf16_decode(ri.x_bits), codecs.bf16_decode(ri.wr_bits)
     r = gating.router_logits(x, wr)
     mag = gating.router_logits(np.abs(x), np.abs(wr))
-    bound = gamma(32 + -(-H // 256) + 16) * mag + 2.0 ** -60
+    # the longest accumulation chain of either router kernel: 32 products inside an MFMA
+    # step, then up to H / 32 chained steps (the LDS-tiled kernel: one wave takes all of
+    # K) or H / 256 steps and 16 wave partials (the kernel for few tokens)
+    bound = gamma(32 + H // 32 + 16) * mag + 2.0 ** -60
     return g, r, bound
 
 
 @pytest.mark.parametrize("T,H,E", [(1, 32, 1), (5, 64, 7), (17, 96, 33), (40, 512, 64),
                                    (33, 1056, 250), (130, 2048, 256),
                                    # wide token tiles (enough tiles to cover the CUs), ragged T and E
-                                   (1000, 256, 256), (2050, 96, 130)])
+                                   (1000, 256, 256), (2050, 96, 130),
+                                   # the LDS-tiled kernel: 5 and 6 K chunks (both peeled tails),
+                                   # ragged T and E, and the full hidden size
+                                   (300, 640, 256), (257, 768, 100), (512, 7168, 256)])
 def test_router_logits_within_fp32_bound(lib, T, H, E):
     g, r, bound = router_case(T, H, E, seed=T * 131 + E)
     err = np.abs(g - r)
@@ -135,9 +141,10 @@ def test_gate_calls_after_empty_batch(lib):
 
 # ---------------------------------------------------------------- fused gate
 def fused_bound(H, mag):
-    # per wave at most ceil(H / 128) chained MFMA steps (K split over >= 1 slice x 4 waves),
-    # 4 wave partials, at most 16 slice partials
-    return gamma(32 + -(-H // 128) + 4 + 16) * mag + 2.0 ** -60
+    # per wave at most H / 32 chained MFMA steps (the LDS-tiled kernel's K slice, at least
+    # one slice; the kernel for few tokens splits K over 4 waves and adds 4 wave
+    # partials), at most 16 slice partials
+    return gamma(32 + H // 32 + 4 + 16) * mag + 2.0 ** -60
 
 
 @pytest.mark.parametrize("T,H,E,k", [(1, 256, 8, 2), (5, 1056, 100, 4), (16, 512, 256, 8), (17, 7168, 256, 8),
@@ -146,7 +153,11 @@ def fused_bound(H, mag):
                                      (1024, 7168, 256, 8), (2, 64, 1, 1),
                                      # 6 and 11 K slices: the top-k re-reads the last slice
                                      # for the missing ones and drops them
-                                     (50, 1536, 64, 4), (100, 2816, 256, 8)])
+                                     (50, 1536, 64, 4), (100, 2816, 256, 8),
+                                     # the LDS-tiled kernel: one K chunk per slice, two slices of
+                                     # five chunks, and 4096 tokens in one slice (the largest
+                                     # shape the no-allocation scratch holds)
+                                     (600, 640, 100, 4), (2048, 1280, 256, 8), (4096, 7168, 256, 8)])
 def test_fused_gate_matches_oracle(lib, T, H, E, k):
     ri = synth.make_router_inputs(T, H, E, seed=7 * T + H + E)
     x, wr = dev_bits(ri.x_bits), dev_bits(ri.wr_bits)
