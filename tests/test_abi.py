@@ -123,8 +123,11 @@ def test_gate_workspace_sizes(lib):
     assert lib.moe_gate_workspace_bytes(4096, 7168, 256) == 4096 * 256 * 4
     # a small batch is split 16 ways too
     assert lib.moe_gate_workspace_bytes(8, 7168, 256) == 16 * 8 * 256 * 4
-    # 512 tokens: 64 tiles, a 4-way split
-    assert lib.moe_gate_workspace_bytes(512, 7168, 256) == 4 * 512 * 256 * 4
+    # from 256 tokens the router runs on 64 x 64 LDS tiles: 512 tokens give 32 tiles, so
+    # K is split 8 ways (about 256 workgroups; 8 x 512 partial rows fit the 4096-row bound)
+    assert lib.moe_gate_workspace_bytes(512, 7168, 256) == 8 * 512 * 256 * 4
+    # 1024 tokens: 64 tiles want a 4-way split, which the 4096-row bound allows
+    assert lib.moe_gate_workspace_bytes(1024, 7168, 256) == 4 * 1024 * 256 * 4
     # a short K cannot be split below 8 steps per slice
     assert lib.moe_gate_workspace_bytes(8, 256, 8) == 8 * 8 * 4
     assert lib.moe_gate_workspace_bytes(100, 2816, 256) == 11 * 100 * 256 * 4
