@@ -34,7 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 # the GEMM1 kernel's source and the headers compiled into it
 GEMM1_SRC = [os.path.join(ROOT, "combine_top_gate_amd", "csrc", f)
-             for f in ("gemm_lowp.hip", "dispatch_chunk.h", "kernels.h", "pack_layout.h")]
+             for f in ("gemm_lowp.hip", "dispatch_chunk.h", "kernels.h", "common.h", "pack_layout.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_decode128_fp8_traffic.md")
 
 
@@ -192,6 +192,23 @@ def time_graph(torch, moe, ds, steps):
     del g
     return {"us_per_call": round(us, 2), "calls": reps * len(ds),
             "method": "HIP graph of one layer call per weight copy, replayed back to back behind a GPU spin"}
+
+
+def time_fused_combine(torch, binding, moe, run, steps):
+    """The layer with the combine formed in GEMM2's epilogue (MOE_OPT_FUSED_COMBINE), over
+    the same steps as the default loop (us per step)."""
+    moe.set_option(binding.MOE_OPT_FUSED_COMBINE, 1)
+    try:
+        for i in range(5):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(i)
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t0) * 1e6 / steps, 2)
+    finally:
+        moe.set_option(binding.MOE_OPT_FUSED_COMBINE, 0)
 
 
 def time_combine_fp8(torch, moe, d, inp, nbytes_combine, calls=200):
@@ -373,6 +390,9 @@ def main():
     dist = layer_distribution(torch, run, args.steps)
     # the SENTINEL handshake's per-call epoch cannot be replayed from a graph
     graph = time_graph(torch, moe, ds, args.steps) if sched == binding.MOE_SCHED_FENCE else None
+    # the decode GEMM2 can also form the combine (an option; the tiled prefill path cannot)
+    fused_combine = (time_fused_combine(torch, binding, moe, run, args.steps)
+                     if args.workload.startswith("decode") else None)
     disp_warm, disp_cold = time_warm_cold(torch, lambda: moe.dispatch(inp.T_s, d.x, d.x_scale, d.ids))
     comb_warm, comb_cold = time_warm_cold(torch, lambda: moe.combine(d.topk_w, d.out))
     if args.calib_copy_mib:
@@ -418,6 +438,7 @@ def main():
         "us_per_step_with_stage_events": round((t3 - t2) * 1e6 / args.steps, 2),
         "layer_us_dist": dist,
         "layer_us_graph": graph,
+        "layer_us_fused_combine": fused_combine,
         "weight_copies": len(ds),
         "dispatch_alone": {"warm_us": round(disp_warm, 2), "cold_us": round(disp_cold, 2),
                            "warm_GBps": round(gbps(nbytes["dispatch"], disp_warm * 1e-3), 1),

@@ -60,6 +60,7 @@ struct moe_ctx {
   uint32_t* sched = nullptr;  // persistent GEMM: queue heads, exit count, per-group counters
   int* plan = nullptr;        // tiled GEMM: tile table and work counters
   uint32_t* sync = nullptr;   // SENTINEL: rflag[MOE_MAX_SRC], dflag[..], arrive[..]
+  uint32_t* ccnt = nullptr;   // combine in GEMM2: [max tokens][ceil(H/256)] counters, zero between calls
   int n_cu = 0;
   // SENTINEL with dispatch_cus > 0: dispatch and GEMM1 streams on disjoint CU sets and
   // their fork/join events; with 0, the dispatch runs inside the GEMM1 launch
@@ -73,6 +74,7 @@ struct moe_ctx {
   uint32_t delay_ticks = 0;     // SENTINEL dispatch delay (100 MHz ticks), a test aid
   // options
   int opt_persistent = 0, opt_tiles = 0, opt_queue = 0, opt_tiled = 0, opt_tiled_m32 = 0;
+  int opt_fcombine = 0;  // the combine in the decode GEMM2's epilogue
   // state of the last dispatch
   int T_s = -1;
   SrcPtrs src{};
@@ -207,12 +209,14 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (e = alloc((void**)&c->err, 4)) != hipSuccess ||
       (e = alloc((void**)&c->sched, kSchedWords * 4)) != hipSuccess ||
       (e = alloc((void**)&c->plan, (size_t)tiled_plan_words() * 4)) != hipSuccess ||
-      (e = alloc((void**)&c->sync, 3 * MOE_MAX_SRC * 4)) != hipSuccess)
+      (e = alloc((void**)&c->sync, 3 * MOE_MAX_SRC * 4)) != hipSuccess ||
+      (e = alloc((void**)&c->ccnt, (size_t)S * Tc * ((H + 255) / 256) * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "workspace allocation failed: %s", hipGetErrorString(e)));
   if ((e = hipMemset(c->err, 0, 4)) != hipSuccess || (e = hipMemset(c->cnt, 0, (size_t)S * E * 4)) != hipSuccess ||
       (e = hipMemset(c->sched, 0, kSchedWords * 4)) != hipSuccess ||
       (e = hipMemset(c->off, 0, (size_t)S * E * 4)) != hipSuccess ||
-      (e = hipMemset(c->sync, 0, 3 * MOE_MAX_SRC * 4)) != hipSuccess)
+      (e = hipMemset(c->sync, 0, 3 * MOE_MAX_SRC * 4)) != hipSuccess ||
+      (e = hipMemset(c->ccnt, 0, (size_t)S * Tc * ((H + 255) / 256) * 4)) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)));
   hipDeviceProp_t prop;
   if ((e = hipGetDeviceProperties(&prop, c->device)) != hipSuccess)
@@ -247,7 +251,7 @@ moe_status moe_destroy(moe_ctx* c) {
   for (hipStream_t st : {c->s_disp, c->s_comp})
     if (st) (void)hipStreamDestroy(st);
   void* bufs[] = {c->win,     c->wsc,     c->h,   c->hs,    c->y,    c->cnt,
-                  c->off,     c->dst_row, c->row_src, c->err, c->sched, c->plan, c->sync};
+                  c->off,     c->dst_row, c->row_src, c->err, c->sched, c->plan, c->sync, c->ccnt};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete c;
@@ -394,8 +398,15 @@ static moe_status poison(moe_ctx* c, hipStream_t stream) {
 // sn: SENTINEL -- GEMM1 polls the dispatch's flags.  fused != null: the dispatch chunks
 // run in the GEMM1 launch itself, on `stream`; otherwise GEMM1 runs on the compute
 // stream and GEMM2 joins both streams back into `stream`.
+// combine != null (moe_layer): {topk_w, out}; with MOE_OPT_FUSED_COMBINE on a path that
+// takes it, GEMM2 also forms the combine and *combined is set.
+struct CombineTarget {
+  const float* topk_w;
+  void* out;
+  bool combined;
+};
 static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t stream, bool timed, bool sn = false,
-                             const DispatchArgs* fused = nullptr) {
+                             const DispatchArgs* fused = nullptr, CombineTarget* combine = nullptr) {
   const moe_config& cf = c->cfg;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (c->T_s < 0) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm before any moe_dispatch");
@@ -493,6 +504,15 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
     HIP_TRY(launch_tiled(ta, c->n_cu, stream));
     if (timed) record(c, 2, stream);
     return MOE_OK;
+  }
+  if (!f32 && combine && c->opt_fcombine) {
+    // the combine in GEMM2's epilogue (the decode kernels, two-kernel or persistent)
+    g.ccnt = c->ccnt;
+    g.dst_row = c->dst_row;
+    g.row_src = c->row_src;
+    g.topk_w = combine->topk_w;
+    g.out = static_cast<uint16_t*>(combine->out);
+    combine->combined = true;
   }
   if (f32 || a16 || !c->opt_persistent || sn) {
     HIP_TRY(f32 ? launch_gemm2_f32(g, stream) : launch_gemm2_lowp(g, wf, packed, nt, stream));
@@ -601,11 +621,14 @@ moe_status moe_layer(moe_ctx* c, int32_t T_s, const void* const* x, const float*
     if (st != MOE_OK) return st;
     if (timed) record(c, 1, stream);
   }
-  st = gemm_stage(c, w, stream, timed, sn, use_fused ? &fused : nullptr);
+  CombineTarget ct{topk_w, out, false};
+  st = gemm_stage(c, w, stream, timed, sn, use_fused ? &fused : nullptr, &ct);
   if (st != MOE_OK) return st;
   if (timed) record(c, 3, stream);
-  st = moe_combine(c, topk_w, out, stream);
-  if (st != MOE_OK) return st;
+  if (!ct.combined) {
+    st = moe_combine(c, topk_w, out, stream);
+    if (st != MOE_OK) return st;
+  }
   if (timed) {
     record(c, 4, stream);
     c->timing_n++;
@@ -772,6 +795,10 @@ moe_status moe_set_option(moe_ctx* c, moe_option opt, int32_t v) {
     case MOE_OPT_DISPATCH_DELAY:
       if (v < 0 || v > kMaxDelayUs) break;
       c->delay_ticks = (uint32_t)v * 100u;  // the real-time counter runs at 100 MHz
+      return MOE_OK;
+    case MOE_OPT_FUSED_COMBINE:
+      if (v != 0 && v != 1) break;
+      c->opt_fcombine = v;
       return MOE_OK;
   }
   return fail(MOE_ERR_INVALID_ARG, "option %d does not take value %d", (int)opt, v);

@@ -73,3 +73,19 @@ __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcp
 // A value of a 1x128 block divided by the block's fp32 scale, clamped to the e4m3 range:
 // inv_sc = __builtin_amdgcn_rcpf(scale), computed once per block (v_rcp_f32, 1 ulp).
 __device__ __forceinline__ float e4m3_scaled(float v, float inv_sc) { return fminf(fmaxf(v * inv_sc, -448.0f), 448.0f); }
+
+// Waits until this wave's vector memory operations, its stores included, have completed
+// (s_waitcnt vmcnt(0): vmcnt 0, expcnt and lgkmcnt not waited for).  A workgroup barrier
+// does not wait for other waves' stores, so before one wave releases the workgroup's
+// stores at agent scope every wave calls this ahead of the barrier.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Makes the workgroup's global stores so far visible at agent scope with a single write-back
+// of the XCD's L2 (issued by wave 0) instead of one per wave.  Every thread calls it; it
+// ends with a barrier, so any thread may then publish with a relaxed agent-scope atomic.
+__device__ __forceinline__ void release_workgroup_stores() {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+}

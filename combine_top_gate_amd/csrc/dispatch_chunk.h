@@ -195,6 +195,7 @@ __device__ __forceinline__ void dispatch_chunk_u(const DispatchArgs& a, int s, i
   if (p == chunks - 1)
     for (int r = total + tid; r < n; r += kDispatchThreads) a.row_src[base + r] = -1;
   if (a.rflag && p == 0) {
+    wait_vmem();  // every wave's count and offset stores are done before thread 0 releases them
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.rflag + s, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -226,6 +227,7 @@ __device__ __forceinline__ void dispatch_chunk_u(const DispatchArgs& a, int s, i
     }
   }
   if (a.dflag) {
+    wait_vmem();  // every wave's window rows are stored before thread 0 releases them
     __syncthreads();
     if (tid == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(a.arrive + s, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);

@@ -806,6 +806,132 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs 
     gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg);
 }
 
+// ------------------------------------------------------------------ combine in GEMM2
+// Option: the top-k weighted combine runs in GEMM2's epilogue instead of as its own
+// kernel (the fused form the pages set against their split design: "GC-MoE:
+// Decoupling MoE Communication and Computation with CUDA Green Contexts", "Why Expert
+// Parallelism Is Inefficient in MoE Decoding").  A work item (group g, output columns
+// nb*256 .. +255) counts, for each of its rows, one contribution of that row's token
+// to those columns: an atomic counter per (token, column block) at agent scope, taken
+// after the item's y stores have been made visible at agent scope (one write-back of the
+// XCD's L2 per item).  The item whose count completes a token's set -- its slots with a
+// row, plus the shared expert's row -- reads the token's y rows, which come from other
+// experts' items on other XCDs, with agent-coherent loads (no L2 invalidation), and
+// forms out[t][nb*256 .. +255] from them with the combine
+// kernel's arithmetic (fp32 FMAs in slot order, the shared row last with weight 1,
+// bf16 rounding), so its output is bit-identical to that kernel's.  It then resets the
+// counter: every counter is back at zero when the launch ends, and no pass clears them
+// between calls.  Tokens with no contribution at all (no slot with a row, no shared
+// expert) get zero rows from workgroups past the last work item.
+
+// Contributions that complete token t: its slots with a window row, plus the shared row.
+__device__ __forceinline__ int token_need(const GemmArgs& p, int t) {
+  const int k = p.d.k;
+  int n = p.d.Ish > 0 ? 1 : 0;
+  for (int j = 0; j < k; ++j) n += p.dst_row[(int64_t)t * k + j] >= 0 ? 1 : 0;
+  return n;
+}
+
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& y, float w) {
+  const uint32_t u[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] = fmaf(w, bf16_to_f32(u[q] & 0xFFFFu), acc[2 * q]);
+    acc[2 * q + 1] = fmaf(w, bf16_to_f32(u[q] >> 16), acc[2 * q + 1]);
+  }
+}
+
+// 16 bytes of a y row written by another work item, read coherently at agent scope (four
+// relaxed agent-scope loads: they miss any stale copy in this XCD's L2, so no L2
+// invalidation is needed).  The caller issues them only after its counter update has seen
+// every writer's, and each writer made its rows visible at agent scope before its update.
+__device__ __forceinline__ uint4 load_coherent16(const uint16_t* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  uint4 v;
+  v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// out[t][c .. c+7] from the token's y rows (one 16-byte piece per lane).
+__device__ __forceinline__ void combine_piece(const GemmArgs& p, int t, int c) {
+  const BatchDims& d = p.d;
+  if (c >= d.H) return;
+  const int k = d.k;
+  const int32_t* rmap = p.dst_row + (int64_t)t * k;
+  const float* wmap = p.topk_w + (int64_t)t * k;
+  const uint16_t* yc = p.y + c;
+  float acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += 8) {  // eight slots' rows in flight at a time, added in slot order
+    int rows[8];
+    uint4 yv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = j0 + j < k ? rmap[j0 + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) yv[j] = load_coherent16(yc + (int64_t)max(rows[j], 0) * d.H);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (rows[j] >= 0) add_bf16x8(acc, yv[j], wmap[j0 + j]);
+  }
+  if (d.Ish) add_bf16x8(acc, load_coherent16(yc + (int64_t)(d.R + t) * d.H), 1.0f);
+  uint4 o;
+  o.x = pack2_bf16(acc[0], acc[1]);
+  o.y = pack2_bf16(acc[2], acc[3]);
+  o.z = pack2_bf16(acc[4], acc[5]);
+  o.w = pack2_bf16(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(p.out + (int64_t)t * d.H + c) = o;
+}
+
+// After a GEMM2 item's passes: count its rows [mb, me) of group g towards their tokens'
+// column block nb and combine the tokens it completes.  Every thread calls it.
+__device__ __forceinline__ void combine_tail(const GemmArgs& p, int g, int nb, int mb, int me, const SegTable& seg) {
+  __shared__ int s_list[256];
+  __shared__ int s_n;
+  const BatchDims& d = p.d;
+  const int nbh = (d.H + 255) >> 8;
+  release_workgroup_stores();  // the item's y rows, visible at agent scope before any count
+  for (int m0 = mb; m0 < me; m0 += 256) {
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    const int m = m0 + (int)threadIdx.x;
+    if (m < me) {
+      const int t = g < d.E ? p.row_src[seg_row(seg, d.S, m)] / d.k : m;
+      uint32_t* cp = p.ccnt + (int64_t)t * nbh + nb;
+      const uint32_t old = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)old + 1 == token_need(p, t)) {
+        __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+        s_list[atomicAdd(&s_n, 1)] = t;
+      }
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int i = (int)threadIdx.x >> 5; i < n; i += 8) combine_piece(p, s_list[i], nb * 256 + 8 * (threadIdx.x & 31));
+    __syncthreads();  // s_n and s_list are reused
+  }
+}
+
+// Workgroups past the last work item: zero output rows of the tokens [b*256, +256) with
+// no contribution (only possible without a shared expert).
+__device__ __forceinline__ void combine_zero_rows(const GemmArgs& p, int b) {
+  __shared__ int s_list[256];
+  __shared__ int s_n;
+  const BatchDims& d = p.d;
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  const int t = b * 256 + (int)threadIdx.x;
+  if (t < d.T && token_need(p, t) == 0) s_list[atomicAdd(&s_n, 1)] = t;
+  __syncthreads();
+  const int n = s_n, per_row = d.H >> 3;
+  for (int i = (int)threadIdx.x; i < n * per_row; i += 256) {
+    const int tt = s_list[i / per_row], c = 8 * (i % per_row);
+    *reinterpret_cast<uint4*>(p.out + (int64_t)tt * d.H + c) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 // ------------------------------------------------------------------ GEMM2
 template <int WFMT, bool PACKED, int NT, bool DIRECT = false>
 __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, PACKED>& ws, const SegTable& t,
@@ -849,7 +975,7 @@ __device__ __forceinline__ void gemm2_pass(const GemmArgs& p, const WSrc<WFMT, P
 
 // One GEMM2 work item: output rows nb*256 .. +255 of expert group g, over all of the
 // group's rows.  Every thread of the workgroup calls it.
-template <int NTMAX, int WFMT, bool PACKED>
+template <int NTMAX, int WFMT, bool PACKED, bool FUSEC = false>
 __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item, float* s_tsc, uint8_t* s_tok,
                                            SegTable& seg) {
   const BatchDims& d = p.d;
@@ -908,17 +1034,26 @@ __device__ __forceinline__ void gemm2_item(const GemmArgs& p, int g, int nb_item
       default: if constexpr (NTMAX >= 6) gemm2_pass<WFMT, PACKED, 6>(p, ws, seg, g, rb, active, K, me, m0, s_tsc, s_tok); break;
     }
   }
+  if constexpr (FUSEC) combine_tail(p, g, nb, mb, me, seg);
 }
 
-template <int NTMAX, int WFMT, bool PACKED>
+template <int NTMAX, int WFMT, bool PACKED, bool FUSEC = false>
 __global__ __launch_bounds__(256, 2) void k_gemm2_lowp(GemmArgs p) {
   __shared__ SegTable seg;
   float* s_tsc = reinterpret_cast<float*>(g_lds);
   uint8_t* s_tok = g_lds + lds_tsc_bytes(p.d.hstride >> 7, NTMAX, kA16<WFMT>);
   const int nbh = (p.d.H + 255) >> 8;  // 256 output rows per workgroup, 64 per wave
+  const int nb_s = p.d.Ish ? nbh * p.sh_chunks : 0;
+  if constexpr (FUSEC) {
+    const int items = p.d.E * nbh + nb_s;
+    if ((int)blockIdx.x >= items) {
+      if (!p.d.Ish) combine_zero_rows(p, (int)blockIdx.x - items);
+      return;
+    }
+  }
   int g, nb;
-  work_item(p.d, nbh, p.d.Ish ? nbh * p.sh_chunks : 0, blockIdx.x, g, nb);
-  gemm2_item<NTMAX, WFMT, PACKED>(p, g, nb, s_tsc, s_tok, seg);
+  work_item(p.d, nbh, nb_s, blockIdx.x, g, nb);
+  gemm2_item<NTMAX, WFMT, PACKED, FUSEC>(p, g, nb, s_tsc, s_tok, seg);
 }
 
 // ------------------------------------------------------------------ persistent
@@ -953,7 +1088,9 @@ __device__ __forceinline__ int decode_item(const ExpertsArgs& a, int q, int step
   return 0;
 }
 
-template <int NTMAX, int WFMT, bool PACKED>
+// FUSEC: the combine runs in the GEMM2 items' epilogue (a.g2.ccnt set), and the zero rows
+// of tokens with no contribution are written by the workgroups as they leave.
+template <int NTMAX, int WFMT, bool PACKED, bool FUSEC = false>
 __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
   __shared__ float s_amax[4][kMaxTok];
   __shared__ int s_item, s_go;
@@ -973,8 +1110,8 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
     if (kind == 0) break;  // uniform over the workgroup
     if (kind == 1) {
       gemm1_item<NTMAX, WFMT, PACKED>(a.g1, g, nb, s_amax, s_tsc, s_tok, seg);
-      __syncthreads();  // every wave's h stores are done
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(done1 + g, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      release_workgroup_stores();  // every wave's h stores, visible at agent scope
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(done1 + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       if (threadIdx.x == 0) {
         const uint32_t need = (uint32_t)items1_of(a, g);
@@ -990,9 +1127,16 @@ __global__ __launch_bounds__(256, 2) void k_experts_lowp(ExpertsArgs a) {
         if (!s_go) atomicOr(a.g1.err, MOE_DEVERR_TIMEOUT);
       }
       __syncthreads();
-      if (s_go) gemm2_item<NTMAX, WFMT, PACKED>(a.g2, g, nb, s_tsc, s_tok, seg);
+      if (s_go) gemm2_item<NTMAX, WFMT, PACKED, FUSEC>(a.g2, g, nb, s_tsc, s_tok, seg);
     }
     __syncthreads();  // s_item, s_go and the LDS tables are free again
+  }
+  if constexpr (FUSEC) {
+    if (!a.g2.d.Ish)
+      for (int tb = (int)blockIdx.x; tb * 256 < a.g2.d.T; tb += (int)gridDim.x) {
+        combine_zero_rows(a.g2, tb);
+        __syncthreads();  // its token list is rebuilt by the next round
+      }
   }
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -1045,33 +1189,52 @@ hipError_t launch1(const GemmArgs& a, int nt, const DispatchArgs* fused, hipStre
   return hipGetLastError();
 }
 
+template <int WFMT, bool PACKED, bool FUSEC>
+void launch2_nt(const GemmArgs& a, int nt, dim3 grid, hipStream_t st) {
+  const int KB = a.d.hstride >> 7;
+  constexpr bool A16 = kA16<WFMT>;
+  const dim3 block(256);
+  if (nt <= 2)
+    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED, FUSEC>), grid, block, lds_bytes(KB, 2, A16), st, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED, FUSEC>), grid, block, lds_bytes(KB, 3, A16), st, a);
+  else if (nt == 4 || !kFp4W<WFMT>)
+    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED, FUSEC>), grid, block, lds_bytes(KB, 4, A16), st, a);
+  else
+    hipLaunchKernelGGL((k_gemm2_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED, FUSEC>), grid, block,
+                       lds_bytes(KB, 5, A16), st, a);
+}
+
+// a.ccnt != null: the combine runs in the epilogue (plus a workgroup per 256 tokens for
+// the zero rows of tokens with no contribution, when there is no shared expert).
 template <int WFMT, bool PACKED>
 hipError_t launch2(const GemmArgs& a, int nt, hipStream_t st) {
   const int nbh = (a.d.H + 255) >> 8;
-  const dim3 grid(a.d.E * nbh + (a.d.Ish ? nbh * a.sh_chunks : 0)), block(256);
-  const int KB = a.d.hstride >> 7;
-  constexpr bool A16 = kA16<WFMT>;
-  if (nt <= 2)
-    hipLaunchKernelGGL((k_gemm2_lowp<2, WFMT, PACKED>), grid, block, lds_bytes(KB, 2, A16), st, a);
-  else if (nt == 3)
-    hipLaunchKernelGGL((k_gemm2_lowp<3, WFMT, PACKED>), grid, block, lds_bytes(KB, 3, A16), st, a);
-  else if (nt == 4 || !kFp4W<WFMT>)
-    hipLaunchKernelGGL((k_gemm2_lowp<4, WFMT, PACKED>), grid, block, lds_bytes(KB, 4, A16), st, a);
+  const int items = a.d.E * nbh + (a.d.Ish ? nbh * a.sh_chunks : 0);
+  if (a.ccnt)
+    launch2_nt<WFMT, PACKED, true>(a, nt, dim3(items + (a.d.Ish ? 0 : (a.d.T + 255) / 256)), st);
   else
-    hipLaunchKernelGGL((k_gemm2_lowp<5, (kFp4W<WFMT> ? WFMT : MOE_FP4_E2M1), PACKED>), grid, block,
-                       lds_bytes(KB, 5, A16), st, a);
+    launch2_nt<WFMT, PACKED, false>(a, nt, dim3(items), st);
   return hipGetLastError();
+}
+
+template <int WFMT, bool PACKED, bool FUSEC>
+void launch_experts_nt(const ExpertsArgs& a, int nt, int grid, hipStream_t st) {
+  const int KB = std::max(a.g1.d.H, a.g1.d.hstride) >> 7;
+  if (nt <= 2)
+    hipLaunchKernelGGL((k_experts_lowp<2, WFMT, PACKED, FUSEC>), dim3(grid), dim3(256), lds_bytes(KB, 2), st, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((k_experts_lowp<3, WFMT, PACKED, FUSEC>), dim3(grid), dim3(256), lds_bytes(KB, 3), st, a);
+  else
+    hipLaunchKernelGGL((k_experts_lowp<4, WFMT, PACKED, FUSEC>), dim3(grid), dim3(256), lds_bytes(KB, 4), st, a);
 }
 
 template <int WFMT, bool PACKED>
 hipError_t launch_experts(const ExpertsArgs& a, int nt, int grid, hipStream_t st) {
-  const int KB = std::max(a.g1.d.H, a.g1.d.hstride) >> 7;
-  if (nt <= 2)
-    hipLaunchKernelGGL((k_experts_lowp<2, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 2), st, a);
-  else if (nt == 3)
-    hipLaunchKernelGGL((k_experts_lowp<3, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 3), st, a);
+  if (a.g2.ccnt)
+    launch_experts_nt<WFMT, PACKED, true>(a, nt, grid, st);
   else
-    hipLaunchKernelGGL((k_experts_lowp<4, WFMT, PACKED>), dim3(grid), dim3(256), lds_bytes(KB, 4), st, a);
+    launch_experts_nt<WFMT, PACKED, false>(a, nt, grid, st);
   return hipGetLastError();
 }
 

@@ -65,6 +65,12 @@ struct GemmArgs {
   const uint32_t* dflag;
   uint32_t epoch;
   uint32_t spin_limit;
+  // GEMM2 with the combine in its epilogue (bf16 y and out); null ccnt: no combine here
+  uint32_t* ccnt;          // [T][ceil(H/256)] contributions counted per token and column block, zero between calls
+  const int32_t* dst_row;  // [T][k] window row of each slot, -1 for none
+  const int32_t* row_src;  // [R] flattened (token, slot) pair of each window row
+  const float* topk_w;     // [T][k]
+  uint16_t* out;           // [T][H]
 };
 // The W4A16 variant of the decode GEMMs: MXFP4 weights (stored as MOE_FP4_E2M1), bf16
 // activations and bf16 h.  Passed as weight_fmt; not a moe_dtype.

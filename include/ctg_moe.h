@@ -278,6 +278,14 @@ moe_status moe_pack_weights(moe_ctx* ctx, const moe_weights* src, const moe_weig
  *                            1: 32x32x64, the two 64-deep halves of a 128-deep scale block
  *                            chained before one promotion (results agree with 0 to fp32
  *                            rounding of the block sums, not bit for bit).
+ *   MOE_OPT_FUSED_COMBINE    1: moe_layer forms the top-k weighted combine in the epilogue
+ *                            of the decode GEMM2 (the weight-streaming kernels, two-kernel
+ *                            or persistent, bf16 out): the item that brings a token's last
+ *                            contribution to a block of 256 output columns sums that block
+ *                            (per-token counters at agent scope, reset by that item), with
+ *                            the combine kernel's arithmetic, so the output is
+ *                            bit-identical; the tiled and fp32 paths keep the combine
+ *                            kernel; 0: the combine kernel (default).
  * Test aids for the handshake and the reuse of the workspace without a clean pass:
  *   MOE_OPT_POISON           1: every moe_layer call first fills the windows, their scales,
  *                            h, its scales and y (all rows of the capacity) with NaN codes
@@ -301,7 +309,8 @@ typedef enum {
   MOE_OPT_TILED_MFMA = 6,
   MOE_OPT_POISON = 7,
   MOE_OPT_EPOCH = 8,
-  MOE_OPT_DISPATCH_DELAY = 9
+  MOE_OPT_DISPATCH_DELAY = 9,
+  MOE_OPT_FUSED_COMBINE = 10
 } moe_option;
 moe_status moe_set_option(moe_ctx* ctx, moe_option opt, int32_t value);
 

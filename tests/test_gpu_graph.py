@@ -35,6 +35,10 @@ CASES = [
     ("decode256_w4a16_shared", dict(S=2, T_s=9, H=384, I=256, E=4, k=2, shared_I=256), {}),
     ("prefill4096_zipf_fp8", dict(S=2, T_s=96, H=512, I=256, E=4, k=2), {binding.MOE_OPT_TILED_GEMM: 1}),
     ("tiny_f32", {}, {}),
+    # the combine in GEMM2's epilogue: its counters are reset by the items, not by a memset
+    ("decode128_fp8", dict(S=3, T_s=9, H=384, I=256, E=6, k=3), {binding.MOE_OPT_FUSED_COMBINE: 1}),
+    ("decode256_mxfp4_shared", dict(S=3, T_s=7, H=384, I=256, E=5, k=2, shared_I=128),
+     {binding.MOE_OPT_FUSED_COMBINE: 1}),
 ]
 
 

@@ -292,7 +292,7 @@ def test_invalid_options():
                      (binding.MOE_OPT_PERSISTENT_GEMM, 2), (binding.MOE_OPT_SENTINEL_SPIN, -1),
                      (binding.MOE_OPT_SENTINEL_STALL, 2), (binding.MOE_OPT_TILED_MFMA, 2),
                      (binding.MOE_OPT_POISON, 2), (binding.MOE_OPT_DISPATCH_DELAY, -1),
-                     (binding.MOE_OPT_DISPATCH_DELAY, 10001), (10, 0)]:
+                     (binding.MOE_OPT_DISPATCH_DELAY, 10001), (binding.MOE_OPT_FUSED_COMBINE, 2), (11, 0)]:
         with pytest.raises(binding.MoeError):
             moe.set_option(opt, val)
 
