@@ -284,11 +284,18 @@ def gpu_state(moe, inp, rows_only=False):
         y = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 2)
         st["y"] = bf16_np(y.view(torch.int16)).reshape(R + T, H)
     else:
+        # rows this call wrote: the routed rows row_src names and, with a shared expert, rows
+        # R..R+T-1; the others hold whatever the workspace held and are not decoded (their
+        # bit patterns may be signalling NaNs)
+        written = np.concatenate([src.reshape(-1) >= 0, np.full(T, inp.shared_I > 0)])
+
+        def f32_rows(buf, width):
+            u = moe.buffer(buf, (R + T) * width * 4).cpu().numpy().view(np.uint32).reshape(R + T, width)
+            return np.where(written[:, None], u, 0).view(np.float32).astype(np.float64)
+
         st["win"] = moe.buffer(binding.MOE_BUF_WINDOW, R * H * 4).cpu().numpy().view(np.float32).reshape(R, H)
-        st["h"] = moe.buffer(binding.MOE_BUF_H, (R + T) * hstride * 4).cpu().numpy().view(
-            np.float32).reshape(R + T, hstride).astype(np.float64)
-        st["y"] = moe.buffer(binding.MOE_BUF_Y, (R + T) * H * 4).cpu().numpy().view(
-            np.float32).reshape(R + T, H).astype(np.float64)
+        st["h"] = f32_rows(binding.MOE_BUF_H, hstride)
+        st["y"] = f32_rows(binding.MOE_BUF_Y, H)
     torch.cuda.synchronize()
     return st
 
