@@ -153,9 +153,12 @@ def time_warm_cold(torch, fn, reps=50):
     return warm, cold
 
 
-def layer_distribution(torch, run, steps):
-    """p10 / p50 / p90 of single layer calls, HIP events between consecutive calls."""
+def layer_distribution(torch, run, steps=200, warm=20):
+    """p10 / p50 / p90 of single layer calls (200 after 20 warm-up calls), HIP events
+    between consecutive calls."""
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(warm):
+        run(i)
     torch.cuda.synchronize()
     evs[0].record()
     for i in range(steps):
@@ -165,7 +168,8 @@ def layer_distribution(torch, run, steps):
     t = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
     q = lambda f: round(t[min(steps - 1, int(f * steps))], 2)
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9),
-            "method": f"{steps} calls, HIP events between consecutive calls (each a queue barrier)"}
+            "method": f"{steps} calls after {warm} warm-up calls, HIP events between consecutive calls "
+                      "(each a queue barrier)"}
 
 
 def time_graph(torch, moe, ds, steps):
@@ -387,7 +391,7 @@ def main():
     if moe.device_error():
         raise RuntimeError("device error during the timed region")
     print("[bench] layer distribution, warm and cold dispatch / combine", file=sys.stderr, flush=True)
-    dist = layer_distribution(torch, run, args.steps)
+    dist = layer_distribution(torch, run)
     # the SENTINEL handshake's per-call epoch cannot be replayed from a graph
     graph = time_graph(torch, moe, ds, args.steps) if sched == binding.MOE_SCHED_FENCE else None
     # the decode GEMM2 can also form the combine (an option; the tiled prefill path cannot)
