@@ -452,6 +452,15 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.sh_chunk_rows = 16 * nt;
   g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
   GemmArgs g1 = g;
+  if (a16 && d.Ish && !c->opt_tiles) {
+    // W4A16: a pass's bf16 MFMA time grows with its token tiles, so the shared expert's
+    // GEMM1 runs in chunks of two tiles, short items that fill the workgroups the routed
+    // items leave idle; GEMM2 keeps chunks of whole passes (measured at the 256-token
+    // layer, shared chunks of 5 / 4 / 3 / 2 / 1 tiles: GEMM1 237.5 / 238 / 247 / 220 /
+    // 216 us, GEMM2 110 / 111 / 115 / 115 / 133 us)
+    g1.sh_chunk_rows = 32;
+    g1.sh_chunks = (d.T + 31) / 32;
+  }
   // many rows per expert: the LDS-tiled, MFMA-bound kernels (FP8 weights)
   const bool tiled = use_tiled(c, d);
   if (sn) {
@@ -470,7 +479,7 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
       HIP_TRY(hipStreamWaitEvent(stream, c->ev_g1, 0));
     }
   } else if (!tiled && (f32 || a16 || !c->opt_persistent)) {
-    HIP_TRY(f32 ? launch_gemm1_f32(g, stream) : launch_gemm1_lowp(g, wf, packed, nt, stream));
+    HIP_TRY(f32 ? launch_gemm1_f32(g1, stream) : launch_gemm1_lowp(g1, wf, packed, nt, stream));
     if (timed) record(c, 2, stream);
   }
   // GEMM2
