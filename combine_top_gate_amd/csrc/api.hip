@@ -452,17 +452,18 @@ static moe_status gemm_stage(moe_ctx* c, const moe_weights* w, hipStream_t strea
   g.sh_chunk_rows = 16 * nt;
   g.sh_chunks = d.Ish ? std::max(1, (d.T + g.sh_chunk_rows - 1) / g.sh_chunk_rows) : 1;
   GemmArgs g1 = g;
-  if (a16 && d.Ish && !c->opt_tiles) {
-    // W4A16: a pass's bf16 MFMA time grows with its token tiles, so the shared expert's
-    // GEMM1 runs in chunks of two tiles, short items that fill the workgroups the routed
-    // items leave idle; GEMM2 keeps chunks of whole passes (measured at the 256-token
-    // layer, shared chunks of 5 / 4 / 3 / 2 / 1 tiles: GEMM1 237.5 / 238 / 247 / 220 /
-    // 216 us, GEMM2 110 / 111 / 115 / 115 / 133 us)
+  // many rows per expert: the LDS-tiled, MFMA-bound kernels (FP8 weights)
+  const bool tiled = use_tiled(c, d);
+  if (d.Ish && !c->opt_tiles && !tiled && !f32 && (sn || a16 || !c->opt_persistent)) {
+    // GEMM1 as its own launch: its shared-expert items run after every routed item (the
+    // kernel's work order), in chunks of two token tiles, short items that spread over
+    // the workgroups the routed items leave; GEMM2 keeps chunks of whole passes.
+    // Measured at the 256-token layers, shared chunks of 5 / 4 / 2 / 1 tiles: GEMM1
+    // MXFP4 171.8 / 157.8 / 147.5 / 147.5 us, W4A16 - / 162.5 / 164.5 / 165.8 us (with
+    // whole-pass chunks among the routed items, as before: 168.8 and 237.5 us)
     g1.sh_chunk_rows = 32;
     g1.sh_chunks = (d.T + 31) / 32;
   }
-  // many rows per expert: the LDS-tiled, MFMA-bound kernels (FP8 weights)
-  const bool tiled = use_tiled(c, d);
   if (sn) {
     g1.rflag = c->sync;
     g1.dflag = c->sync + MOE_MAX_SRC;

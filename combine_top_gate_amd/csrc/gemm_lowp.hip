@@ -438,15 +438,32 @@ __device__ __forceinline__ void stage_token_scales(float* s_tsc, const float* co
 }
 
 // Flat work list: routed expert g has nb_r entries, then the shared expert nb_s.
-__device__ __forceinline__ void work_item(const BatchDims& d, int nb_r, int nb_s, int b, int& g, int& nb) {
-  const int total = d.E * nb_r + nb_s;
-  const int L = xcd_remap(b, total);
-  if (L < d.E * nb_r) {
+// routed_first (GEMM1): workgroups 0 .. E*nb_r-1 take the routed entries and the later
+// ones the shared expert's, each range spread over the XCDs on its own, so that when the
+// routed entries fill the GPU the shared expert's short chunks run after all of them
+// (and a routed expert with a second pass starts in the first round) instead of routed
+// entries being left for a second round.
+__device__ __forceinline__ void work_item(const BatchDims& d, int nb_r, int nb_s, int b, int& g, int& nb,
+                                          bool routed_first = false) {
+  const int nr = d.E * nb_r;
+  if (routed_first) {
+    if (b < nr) {
+      const int L = xcd_remap(b, nr);
+      g = L / nb_r;
+      nb = L - g * nb_r;
+    } else {
+      g = d.E;
+      nb = xcd_remap(b - nr, nb_s);
+    }
+    return;
+  }
+  const int L = xcd_remap(b, nr + nb_s);
+  if (L < nr) {
     g = L / nb_r;
     nb = L - g * nb_r;
   } else {
     g = d.E;
-    nb = L - d.E * nb_r;
+    nb = L - nr;
   }
 }
 
@@ -798,7 +815,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm1_lowp(GemmArgs p, DispatchArgs 
     }
   }
   int g, nb;
-  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, b, g, nb);
+  work_item(p.d, p.d.I >> 7, (p.d.Ish >> 7) * p.sh_chunks, b, g, nb, true);
   if constexpr (FUSED)
     gemm1_item<NTMAX, WFMT, PACKED>(p, g, nb, s_amax, s_tsc, s_tok, seg,
                                     DispatchPrologue{da, b < nchunks ? b : -1, chunks});
