@@ -232,6 +232,7 @@ __device__ __forceinline__ void compute_slab_a16(v4f (&acc)[4][NT], const u32x4 
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[mt][nt], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);  // one k group's decoded weights live at a time
   }
 }
 
