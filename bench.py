@@ -347,7 +347,9 @@ def main():
     d = binding.DeviceInputs(inp)
     sched = binding.MOE_SCHED_SENTINEL if args.sched == "sentinel" else binding.MOE_SCHED_FENCE
     moe = binding.Moe.for_inputs(inp, sched=sched, dispatch_cus=args.dispatch_cus)
-    if not args.row_major:
+    # fp32 weights have no packed form: the fp32 layer always reads them row-major
+    row_major = args.row_major or inp.weight == "f32"
+    if not row_major:
         # one-time weight preparation (as at model load), outside the timed region
         moe.pack(d)
         torch.cuda.synchronize()
@@ -357,7 +359,7 @@ def main():
     ds = [d]
     if wbytes < 4 * MALL_BYTES:
         d2 = binding.DeviceInputs(inp)
-        if not args.row_major:
+        if not row_major:
             moe.pack(d2)
         ds.append(d2)
         torch.cuda.synchronize()
@@ -428,7 +430,7 @@ def main():
                    "tokens": inp.S * inp.T_s, "hidden": inp.H, "inter": inp.I, "experts": inp.E,
                    "topk": inp.k, "weights": inp.weight, "shared_inter": inp.shared_I,
                    "routing": inp.extra.get("routing"), "schedule": args.sched,
-                   "weight_layout": "row-major" if args.row_major else "packed"},
+                   "weight_layout": "row-major" if row_major else "packed"},
         "stages_us": {"dispatch": round(avg[0] * 1e3, 2), "gemm1": round(avg[1] * 1e3, 2),
                       "gemm2": round(avg[2] * 1e3, 2), "combine": round(avg[3] * 1e3, 2),
                       "layer_events": round(avg[4] * 1e3, 2)},

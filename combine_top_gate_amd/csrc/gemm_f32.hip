@@ -1,12 +1,17 @@
 // Grouped GEMMs of the fp32 layer (no quantisation): h = silu(x W13g^T) * (x W13u^T)
 // kept fp32, then y = h W2^T in fp32.  A plain FMA kernel: this layer is small, and it
 // is here for the fp32 configuration's parity, not for speed.  Same work list as the
-// low-precision kernels: routed experts, then the shared expert (group E).
+// low-precision kernels (routed experts, then the shared expert, group E), with a group's
+// rows also spread over kRowSets workgroups (grid.y), since a small layer has few
+// groups.  Each thread owns one output column of a row and walks its weight row and the
+// token row in 16-byte pieces into four partial sums (one per lane of the piece), added
+// pairwise at the end, so its loads are not serialised behind one chain of FMAs.
 #include "kernels.h"
 
 namespace {
 
-constexpr int kCols = 64;  // output columns per workgroup; 4 token rows at a time
+constexpr int kCols = 64;     // output columns per workgroup; 4 token rows at a time
+constexpr int kRowSets = 8;  // workgroups per column block, each taking every 8th group of 4 rows
 
 __device__ __forceinline__ void group_of(const BatchDims& d, int nb_r, int nb_s, int& g, int& nb) {
   const int L = blockIdx.x;
@@ -27,6 +32,27 @@ __device__ __forceinline__ int rows_of(const GemmArgs& p, int g) {
   return M;
 }
 
+// sum over c < K of a[c] * b[c] (K a multiple of 4, rows 16-byte aligned), as four
+// partial sums over the lanes of 16-byte pieces, added pairwise.
+__device__ __forceinline__ float dot4(const float* a, const float* b, int K) {
+  const float4* a4 = reinterpret_cast<const float4*>(a);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < (K >> 2); ++c) {
+    const float4 x = a4[c], y = b4[c];
+    s0 = fmaf(x.x, y.x, s0);
+    s1 = fmaf(x.y, y.y, s1);
+    s2 = fmaf(x.z, y.z, s2);
+    s3 = fmaf(x.w, y.w, s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// this thread's first row and row step: rows of 4 per workgroup, kRowSets workgroups
+__device__ __forceinline__ int first_row() { return blockIdx.y * (256 / kCols) + threadIdx.x / kCols; }
+constexpr int kRowStep = kRowSets * (256 / kCols);
+
 __global__ __launch_bounds__(256) void k_gemm1_f32(GemmArgs p) {
   const BatchDims& d = p.d;
   int g, nb;
@@ -40,7 +66,7 @@ __global__ __launch_bounds__(256) void k_gemm1_f32(GemmArgs p) {
   const float* wu = W + (int64_t)(inter + n) * d.H;
   const int seg = d.T_s * d.k;
   float* h = reinterpret_cast<float*>(p.h);
-  for (int m = threadIdx.x / kCols; m < M; m += 256 / kCols) {
+  for (int m = first_row(); m < M; m += kRowStep) {
     const float* x;
     int orow;
     if (shared) {
@@ -51,11 +77,7 @@ __global__ __launch_bounds__(256) void k_gemm1_f32(GemmArgs p) {
       orow = routed_row(p.cnt, p.off, d.S, d.E, seg, g, m);
       x = reinterpret_cast<const float*>(p.a) + (int64_t)orow * d.H;
     }
-    float ag = 0.f, au = 0.f;
-    for (int c = 0; c < d.H; ++c) {
-      ag = fmaf(x[c], wg[c], ag);
-      au = fmaf(x[c], wu[c], au);
-    }
+    const float ag = dot4(x, wg, d.H), au = dot4(x, wu, d.H);
     h[(int64_t)orow * d.hstride + n] = silu(ag) * au;
   }
 }
@@ -72,25 +94,23 @@ __global__ __launch_bounds__(256) void k_gemm2_f32(GemmArgs p) {
   const float* wr = W + (int64_t)n * K;
   const int seg = d.T_s * d.k;
   const float* hbuf = reinterpret_cast<const float*>(p.a);
-  for (int m = threadIdx.x / kCols; m < M; m += 256 / kCols) {
+  for (int m = first_row(); m < M; m += kRowStep) {
     const int r = shared ? d.R + m : routed_row(p.cnt, p.off, d.S, d.E, seg, g, m);
     const float* h = hbuf + (int64_t)r * d.hstride;
-    float acc = 0.f;
-    for (int c = 0; c < K; ++c) acc = fmaf(h[c], wr[c], acc);
-    p.yf[(int64_t)r * d.H + n] = acc;
+    p.yf[(int64_t)r * d.H + n] = dot4(h, wr, K);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm1_f32(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.d.E * (a.d.I / kCols) + a.d.Ish / kCols);
+  const dim3 grid(a.d.E * (a.d.I / kCols) + a.d.Ish / kCols, kRowSets);
   hipLaunchKernelGGL(k_gemm1_f32, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_f32(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.d.E * (a.d.H / kCols) + (a.d.Ish ? a.d.H / kCols : 0));
+  const dim3 grid(a.d.E * (a.d.H / kCols) + (a.d.Ish ? a.d.H / kCols : 0), kRowSets);
   hipLaunchKernelGGL(k_gemm2_f32, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
