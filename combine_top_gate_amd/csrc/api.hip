@@ -960,6 +960,12 @@ moe_status moe_last_device_error(moe_ctx* c, uint32_t* bits) {
   HIP_TRY(hipDeviceSynchronize());
   HIP_TRY(hipMemcpy(bits, c->err, 4, hipMemcpyDeviceToHost));
   HIP_TRY(hipMemset(c->err, 0, 4));
+  if (*bits & MOE_DEVERR_TIMEOUT) {
+    // a GEMM2 item the persistent kernel skipped never counted its rows: start the fused
+    // combine's counters from zero again (the device is idle)
+    const size_t nbh = (size_t)(c->cfg.hidden + 255) / 256;
+    HIP_TRY(hipMemset(c->ccnt, 0, (size_t)c->cfg.n_src * c->cfg.max_tokens * nbh * 4));
+  }
   return MOE_OK;
 }
 

@@ -395,7 +395,10 @@ int64_t moe_mfma_fp8_probe(float* sink, int32_t blocks, int32_t iters, hipStream
  */
 moe_status moe_mfma_dot16x16(moe_dtype a_fmt, const uint8_t* a, const uint8_t* b, float* out, hipStream_t stream);
 
-/* Waits for the device, returns the latched device error bits and clears them. */
+/* Waits for the device, returns the latched device error bits and clears them.  After a
+ * timeout (MOE_DEVERR_TIMEOUT) the calls since the last check produced invalid output, and
+ * a persistent GEMM that skipped work may have left the combine counters of
+ * MOE_OPT_FUSED_COMBINE part-counted: this call then also resets them. */
 moe_status moe_last_device_error(moe_ctx* ctx, uint32_t* bits);
 
 /*

@@ -175,3 +175,31 @@ def test_fused_combine_soak(name, over, sched, dcu):
             raise AssertionError(f"call {i} (input set {j}, T_s {dd.inp.T_s}): {bad} outputs differ")
     torch.cuda.synchronize()
     assert fused.device_error() == 0 and ref.device_error() == 0
+
+
+def test_timeout_is_latched_and_the_next_calls_are_right():
+    """A SENTINEL wait forced to give up (invalid output, MOE_DEVERR_TIMEOUT latched) with
+    the combine in GEMM2's epilogue: reading the error word leaves the counters at zero, so
+    the following calls equal the FENCE path with the combine kernel."""
+    inp = synth.make_inputs("decode128_fp8", S=2, T_s=3, H=256, I=128, E=4, k=2, seed=310)
+    ref = binding.Moe.for_inputs(inp)
+    dr = binding.DeviceInputs(inp)
+    ref.run(dr)
+    torch.cuda.synchronize()
+    want = dr.out.clone()
+    ms = binding.Moe.for_inputs(inp, sched=binding.MOE_SCHED_SENTINEL)
+    ms.set_option(FC, 1)
+    d = binding.DeviceInputs(inp)
+    ms.set_option(binding.MOE_OPT_SENTINEL_SPIN, 64)
+    ms.set_option(binding.MOE_OPT_SENTINEL_STALL, 1)
+    ms.run(d)
+    torch.cuda.synchronize()
+    assert ms.device_error() & binding.MOE_DEVERR_TIMEOUT
+    ms.set_option(binding.MOE_OPT_SENTINEL_STALL, 0)
+    ms.set_option(binding.MOE_OPT_SENTINEL_SPIN, 0)
+    for _ in range(3):
+        d.out.fill_(float("nan"))
+        ms.run(d)
+        torch.cuda.synchronize()
+        assert ms.device_error() == 0
+        assert torch.equal(want, d.out)
